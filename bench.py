@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Paged decode attention throughput on one MI355X (gfx950).
+
+One step = one pass of the hot path over one batch: the step's copy-on-write
+block copies (if the workload has any), kv_cache_write of the step's new
+tokens, and paged_attention over every sequence.  The host block allocator ran
+before the timed region (its per-step cost is timed separately and reported
+as ``host_alloc_us``); inputs are resident in HBM when timing starts.
+
+Default workload: Llama-3-8B-shaped GQA decode (256 sequences, contexts
+log-uniform in [64, 8192], 32 query / 8 KV heads, head_dim 128, bf16,
+16-token blocks placed by a seeded permutation of a 2x pool).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+WORKLOAD_NAMES = {
+    "c1": "tiny paged decode: 4 seqs (1,17,33,50), 4 heads MHA, head_dim 64, fp32",
+    "c2": "LLaMA-13B-shaped decode layer: 64 seqs, context U[128,2048], 40/40 heads, head_dim 128, fp16",
+    "c3": "Llama-3-8B-shaped GQA decode: 256 seqs, context log-uniform [64,8192], 32q/8kv heads, head_dim 128, bf16",
+    "c4": "shared-prefix parallel sampling: 64 seqs share a 10000-token prefix + U[0,256] private tails, CoW, 32q/8kv, bf16",
+    "c5": "mixed chunked-prefill + decode: 16 chunks q U[16,512] over context U[0,32768] + 128 decodes U[64,8192], 32q/8kv, bf16",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(spec):
+    """Bytes the method must move per paged_attention call (each KV element once
+    per KV-head group, plus Q, the output and the block-table entries)."""
+    e = spec.elem_bytes
+    n = spec.seq_lens.astype(np.int64)
+    kv = int(n.sum()) * spec.num_kv_heads * spec.head_dim * 2 * e
+    qo = spec.num_q_tokens * spec.num_q_heads * spec.head_dim * e * 2
+    table = int((-(-n // 16)).sum()) * 4
+    return kv, kv + qo + table
+
+
+def cpu_baseline(spec, out_bits, target_s):
+    """The oracle (as it stands) on a bounded sample of the same workload."""
+    import threadpoolctl
+
+    from oracle import allocator as oalloc
+    from oracle import attention as oattn
+    from oracle import numerics
+    from tests import oracle_pipeline as op
+    import workloads
+
+    S = spec.num_seqs
+    sample = list(range(0, S, 8)) if S >= 64 else list(range(S))
+    model = oalloc.BlockAllocatorModel(spec.num_blocks, free_order=spec.free_order)
+    flow = workloads.run_flow(spec, model)
+    log(f"cpu baseline: building oracle pools for {len(sample)} sampled sequences")
+    kp, vp = op.build_pools(spec, flow, seqs=sample)
+    tables = flow.padded_tables(pad=0)
+    q = spec.all_q_bits()
+    qsl = spec.query_start_loc
+    reps, elapsed, ref = 0, 0.0, None
+    while elapsed < target_s and reps < 50:
+        t0 = time.perf_counter()
+        ref = oattn.paged_attention(q, kp, vp, tables, spec.seq_lens, qsl, spec.scale, spec.dtype,
+                                    seqs=sample)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    kv_sample = int(spec.seq_lens[sample].sum()) * spec.num_kv_heads * spec.head_dim * 2 * spec.elem_bytes
+    tok_sample = int(sum(qsl[s + 1] - qsl[s] for s in sample))
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    # parity of the GPU rows of the sample against the oracle
+    got = numerics.to_f64(out_bits, spec.dtype).reshape(ref.shape)
+    rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in sample])
+    diff = np.abs(got[rows] - ref[rows])
+    if spec.dtype == "f32":
+        worst = float((diff.max(axis=-1) / np.abs(ref[rows]).max(axis=-1)).max())
+        ok = worst <= 1e-5
+    else:
+        worst = float(diff.max())
+        ok = worst <= 1e-2
+    base = {
+        "value": round(kv_sample * reps / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(tok_sample * reps / elapsed, 2),
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(sample)} of {S} sequences (every 8th), {int(spec.seq_lens[sample].sum())} context tokens, "
+                  f"{reps} pass(es) in {elapsed:.1f} s, fp64 NumPy",
+    }
+    parity = {"rows": int(len(rows)), "worst": worst, "ok": bool(ok),
+              "tolerance": "1e-5 row-relative" if spec.dtype == "f32" else "1e-2 absolute"}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this path runs on a single MI355X with no sharding "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from paged_kv_cache_446_amd import ops
+    from paged_kv_cache_446_amd.allocator import BlockAllocator
+    from tests.gpu_pipeline import dev_bits, host_bits
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    spec = workloads.named_spec(args.config)
+    log(f"workload {args.config}: S={spec.num_seqs} context tokens={int(spec.seq_lens.sum())} "
+        f"pool blocks={spec.num_blocks}")
+
+    # ---- host allocator (a1): timed on its own ----------------------------
+    alloc = BlockAllocator(spec.num_blocks, free_order=spec.free_order)
+    flow = workloads.run_flow(spec, alloc)
+    # per-step host cost: one batched append of the step's tokens on a copy of the state
+    probe = BlockAllocator(spec.num_blocks, free_order=spec.free_order)
+    pflow_tables = np.stack([t.copy() for t in workloads.run_flow(spec, probe).tables])
+    S = spec.num_seqs
+    nblk = np.array([-(-int(c) // 16) for c in spec.seq_lens], dtype=np.int32)
+    lens = spec.seq_lens.astype(np.int32).copy()
+    t0 = time.perf_counter()
+    probe.batch_append_slots(pflow_tables, nblk, lens, np.ones(S, np.int32))
+    host_alloc_us = (time.perf_counter() - t0) * 1e6
+
+    # ---- device state -------------------------------------------------------
+    elems = spec.num_layers * spec.num_blocks * spec.num_kv_heads * 16 * spec.head_dim
+    tdt = torch.int16 if spec.elem_bytes == 2 else torch.int32
+    poison = np.array([workloads.POISON[spec.dtype]], dtype=workloads.DTYPES[spec.dtype][0]).view(
+        np.int16 if spec.elem_bytes == 2 else np.int32)[0]
+    kp = torch.full((elems,), int(poison), dtype=tdt, device=dev)
+    vp = torch.full((elems,), int(poison), dtype=tdt, device=dev)
+    cache = ops.PagedCache(kp, vp, spec.num_kv_heads, spec.head_dim, dtype=spec.dtype)
+    t0 = time.perf_counter()
+    for ph in flow.setup:
+        if len(ph.pairs):
+            ops.copy_blocks(cache, torch.from_numpy(ph.pairs.copy()).to(dev))
+        for slots, k, v in workloads.iter_phase_chunks(spec, ph, max_tokens=1 << 15):
+            ops.kv_cache_write(cache, dev_bits(k, spec.dtype), dev_bits(v, spec.dtype),
+                               torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    log(f"cached context written in {time.perf_counter() - t0:.1f} s")
+    stp = flow.step
+    step_pairs = torch.from_numpy(stp.pairs.copy()).to(dev) if len(stp.pairs) else None
+    step_slots = torch.from_numpy(stp.slots).to(dev)
+    ks, vs = workloads.step_kv_bits(spec)
+    k_step, v_step = dev_bits(ks, spec.dtype), dev_bits(vs, spec.dtype)
+    tables = torch.from_numpy(flow.padded_tables(pad=0)).to(dev)
+    seq_lens = torch.from_numpy(spec.seq_lens.astype(np.int32)).to(dev)
+    qsl = torch.from_numpy(spec.query_start_loc).to(dev)
+    q = dev_bits(spec.all_q_bits(), spec.dtype)
+    out = torch.zeros_like(q)
+    max_q, max_n = int(spec.q_lens.max()), int(spec.seq_lens.max())
+    ws = torch.empty(ops.workspace_bytes(S, spec.num_q_tokens, max_n, spec.num_q_heads, spec.head_dim),
+                     dtype=torch.uint8, device=dev)
+
+    def attention():
+        ops.paged_attention(cache, out, q, tables, seq_lens, qsl, num_q_heads=spec.num_q_heads,
+                            max_q_len=max_q, max_seq_len=max_n, scale=spec.scale, workspace=ws)
+
+    def step(ev_a=None, ev_b=None):
+        if step_pairs is not None:
+            ops.copy_blocks(cache, step_pairs)
+        ops.kv_cache_write(cache, k_step, v_step, step_slots)
+        if ev_a is not None:
+            ev_a.record()
+        attention()
+        if ev_b is not None:
+            ev_b.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(ev_a[i], ev_b[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = start.elapsed_time(end) / K
+    attn_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    attn_avg = float(np.mean(attn_ms))
+    log(f"{K} steps: {ms_step * 1e3:.1f} us/step (GPU events), wall {wall / K * 1e6:.1f} us/step, "
+        f"attention {attn_avg * 1e3:.1f} us (min {min(attn_ms) * 1e3:.1f})")
+
+    kv_bytes, attn_bytes = algorithmic_bytes(spec)
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = attn_bytes / (attn_avg * 1e-3) / 1e9
+    result = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) + tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/Q, seeded block placement)",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.config],
+            "num_seqs": S,
+            "query_tokens": spec.num_q_tokens,
+            "context_tokens": int(spec.seq_lens.sum()),
+            "num_q_heads": spec.num_q_heads,
+            "num_kv_heads": spec.num_kv_heads,
+            "head_dim": spec.head_dim,
+            "block_size": 16,
+            "pool_blocks": spec.num_blocks,
+            "step": "copy_blocks (CoW pairs, if any) + kv_cache_write + paged_attention",
+        },
+        "tokens_per_s": round(spec.num_q_tokens / (ms_step * 1e-3), 1),
+        "context_tokens_per_s": round(int(spec.seq_lens.sum()) / (ms_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "host_alloc_us": round(host_alloc_us, 1),
+        "roofline": {
+            "kernel": "paged_attention (decode partition kernel + partition merge)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "avg_launch_us": round(attn_avg * 1e3, 2),
+        },
+    }
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(spec, host_bits(out, spec.dtype), args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity_sample"] = parity
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

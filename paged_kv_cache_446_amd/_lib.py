@@ -1,0 +1,101 @@
+"""ctypes loader for libpkv.so: argument marshalling only.
+
+The library is built in-tree (``python -m paged_kv_cache_446_amd.build``).  If it
+is missing, importing the binding raises: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK = 0
+STATUS = {
+    0: "PKV_OK",
+    -1: "PKV_ERR_INVALID_ARGUMENT",
+    -2: "PKV_ERR_UNSUPPORTED",
+    -3: "PKV_ERR_OUT_OF_BLOCKS",
+    -4: "PKV_ERR_REFCOUNT",
+    -5: "PKV_ERR_WORKSPACE",
+    -6: "PKV_ERR_HIP",
+}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+# every symbol include/pkv.h declares
+EXPORTS = (
+    "pkv_status_string", "pkv_pool_bytes", "pkv_kv_cache_write", "pkv_copy_blocks",
+    "pkv_paged_attention", "pkv_paged_attention_workspace_bytes", "pkv_ba_create",
+    "pkv_ba_destroy", "pkv_ba_alloc", "pkv_ba_incref", "pkv_ba_decref", "pkv_ba_refcount",
+    "pkv_ba_num_free", "pkv_ba_num_blocks", "pkv_blocks_for_tokens", "pkv_seq_append_slots",
+    "pkv_batch_append_slots", "pkv_seq_make_writable", "pkv_seq_fork", "pkv_seq_free",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{where}: {self.name}")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("num_layers", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libpkv.so is not built ({LIB_PATH}); run python -m paged_kv_cache_446_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, sz, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    pcache = ctypes.POINTER(CacheDesc)
+    sigs = {
+        "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "pkv_pool_bytes": (sz, [pcache]),
+        "pkv_kv_cache_write": (ctypes.c_int, [pcache, i32, P, P, P, i32, P]),
+        "pkv_copy_blocks": (ctypes.c_int, [pcache, P, i32, P]),
+        "pkv_paged_attention": (ctypes.c_int, [pcache, i32, P, P, P, i32, P, P, i32, i32, i32, i32,
+                                               i32, f32, P, sz, P]),
+        "pkv_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "pkv_ba_create": (ctypes.c_int, [i32, i32, pi32, ctypes.POINTER(P)]),
+        "pkv_ba_destroy": (None, [P]),
+        "pkv_ba_alloc": (ctypes.c_int, [P, pi32]),
+        "pkv_ba_incref": (ctypes.c_int, [P, i32]),
+        "pkv_ba_decref": (ctypes.c_int, [P, i32]),
+        "pkv_ba_refcount": (ctypes.c_int, [P, i32, pi32]),
+        "pkv_ba_num_free": (i32, [P]),
+        "pkv_ba_num_blocks": (i32, [P]),
+        "pkv_blocks_for_tokens": (i64, [i64, i32]),
+        "pkv_seq_append_slots": (ctypes.c_int, [P, pi32, i32, pi32, pi32, i32, pi64, pi32, pi32]),
+        "pkv_batch_append_slots": (ctypes.c_int, [P, pi32, i32, pi32, pi32, pi32, i32, pi64, pi32,
+                                                  pi32, pi32]),
+        "pkv_seq_make_writable": (ctypes.c_int, [P, pi32, i32, i32, pi32, pi32]),
+        "pkv_seq_fork": (ctypes.c_int, [P, pi32, i32, pi32]),
+        "pkv_seq_free": (ctypes.c_int, [P, pi32, i32]),
+    }
+    for name in EXPORTS:
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = sigs[name]
+    _lib = lib
+    return lib
+
+
+def check(status: int, where: str):
+    if status != PKV_OK:
+        raise PkvError(status, where)
