@@ -15,10 +15,16 @@
 // For every 16-token block: 16x16x32 matrix instructions for S^T, a
 // wavefront-shuffle online softmax (running max and sum per column), and
 // 16x16x16 matrix instructions for O^T += V^T . P^T, whose P^T operand is the
-// S^T result already in place.  Decode splits the context of a sequence into
-// partitions of kPartBlocks blocks; the four wavefronts of a workgroup take
-// every fourth block of one partition, merge through LDS, and a second kernel
-// merges partitions with the log-sum-exp rule.
+// S^T result already in place.
+//
+// Decode splits the context of a sequence into partitions of kPartBlocks
+// blocks (1024 tokens).  One workgroup per (sequence, partition, KV head):
+// its four wavefronts take every fourth block, streaming K/V tiles with
+// non-temporal loads (each tile is read once), merge through LDS, and a
+// second kernel merges the partitions of long sequences with the log-sum-exp
+// rule.  Workgroup ids are remapped so that the eight KV heads of one
+// partition, and neighbouring partitions, run on the same XCD (hardware
+// dispatch deals consecutive workgroups round-robin over the eight XCDs).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -29,7 +35,12 @@
 namespace pkv {
 
 constexpr int kWaves = 4;        // wavefronts per workgroup
-constexpr int kPartBlocks = 32;  // blocks per decode partition (512 tokens)
+constexpr int kPartBlocks = 64;  // blocks per decode partition (1024 tokens)
+constexpr int kPerWave = kPartBlocks / kWaves;  // blocks of a partition per wavefront
+constexpr int kXcds = 8;         // accelerator complex dies of an MI355X
+static_assert(kPerWave <= 64, "one block-table entry per lane");
+
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
 
 template <class DT, int D>
 struct Geo {
@@ -60,7 +71,10 @@ __device__ __forceinline__ void load_q(WaveState<DT, D>& st, const typename DT::
   st.l = 0.f;
 }
 
-template <class DT, int D>
+// One (block, KV head) tile of K and of V into registers: chunk i*64 + lane of
+// each.  kStream marks tiles read exactly once (decode): non-temporal loads
+// keep them from displacing reusable lines in the caches.
+template <class DT, int D, bool kStream = false>
 __device__ __forceinline__ void load_tile(const typename DT::T* kt, const typename DT::T* vt,
                                           u32x4 (&kr)[Geo<DT, D>::kChunks],
                                           u32x4 (&vr)[Geo<DT, D>::kChunks], int lane) {
@@ -68,10 +82,20 @@ __device__ __forceinline__ void load_tile(const typename DT::T* kt, const typena
   const u32x4* v4 = (const u32x4*)vt;
 #pragma unroll
   for (int i = 0; i < Geo<DT, D>::kChunks; ++i) {
-    kr[i] = k4[i * kWave + lane];
-    vr[i] = v4[i * kWave + lane];
+    if constexpr (kStream) {
+      kr[i] = __builtin_bit_cast(u32x4, __builtin_nontemporal_load((const u32v4*)(k4 + i * kWave + lane)));
+      vr[i] = __builtin_bit_cast(u32x4, __builtin_nontemporal_load((const u32v4*)(v4 + i * kWave + lane)));
+    } else {
+      kr[i] = k4[i * kWave + lane];
+      vr[i] = v4[i * kWave + lane];
+    }
   }
 }
+
+template <class DT, int D>
+struct TileBuf {
+  u32x4 k[Geo<DT, D>::kChunks], v[Geo<DT, D>::kChunks];
+};
 
 __device__ __forceinline__ float lanef(const u32x4& v, int e) {
   return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
@@ -180,19 +204,50 @@ __device__ __forceinline__ void store_elem(typename DT::T* out, int64_t i, float
 }
 
 // ---------------------------------------------------------------------------
-// Decode: grid (num_kv_heads * max_parts, num_seqs), 4 wavefronts.
+// Decode: a 1-D grid over (sequence, partition, KV head), 4 wavefronts each.
 // ---------------------------------------------------------------------------
+
+// Waves per SIMD the register allocation must allow: three for the 16-bit
+// types up to head_dim 128 (enough K/V bytes in flight per CU), otherwise
+// whatever the kernel needs.
+template <class DT, int D>
+constexpr int decode_occupancy() {
+  return (DT::kBytes == 2 && D <= 128) ? 3 : 1;
+}
+
+// Workgroup id -> work item.  Dispatch deals consecutive ids round-robin over
+// the XCDs; item j = (id % 8) * (grid / 8) + id / 8 gives every XCD one
+// contiguous run of items (the host pads the grid to a multiple of 8).
+__device__ __forceinline__ int xcd_item(int id, int grid) {
+  return (id % kXcds) * (grid / kXcds) + id / kXcds;
+}
+
 template <class DT, int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(
-    const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
-    const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
-    const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ qsl, int num_kv_heads, float scale_log2, int max_parts,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_occupancy<DT, D>())))
+void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
+                   const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
+                   const int32_t* __restrict__ bt, int bt_stride,
+                   const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
+                   int num_seqs, int num_kv_heads, float scale_log2, int max_parts,
+                   float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   typedef Geo<DT, D> Gm;
-  const int s = blockIdx.y;
-  const int h = blockIdx.x % num_kv_heads;
-  const int part = blockIdx.x / num_kv_heads;
+  const int j = xcd_item(blockIdx.x, gridDim.x);
+  const int h = j % num_kv_heads;
+  const int sp = j / num_kv_heads;
+  const int part = sp % max_parts;
+  const int s = sp / max_parts;
+  if (s >= num_seqs) return;  // grid padding
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int b0 = part * kPartBlocks;
+  const int32_t* btr = bt + (int64_t)s * bt_stride;
+  // block-table entries of this wavefront's blocks b0 + w + 4i, one per lane,
+  // loaded alongside the sequence metadata (bounded by the table width only)
+  int btv = 0;
+  {
+    const int bi = b0 + w + kWaves * lane;
+    if (lane < kPerWave && bi < bt_stride) btv = btr[bi];
+  }
   const int qb = qsl[s];
   if (qsl[s + 1] - qb != 1) return;
   const int n = seq_lens[s];
@@ -205,40 +260,34 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
   // a sequence longer than the bounds the host passed is cut at them (never read past them)
   const int nblocks = min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks));
-  const int b0 = part * kPartBlocks;
   if (b0 >= nblocks) return;
   const int b1 = min(nblocks, b0 + kPartBlocks);
   const int nparts = (nblocks + kPartBlocks - 1) / kPartBlocks;
-
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
 
   WaveState<DT, D> st;
   load_q<DT, D>(st, q + ((int64_t)qb * hq + h * G + (c < G ? c : 0)) * D, c < G, g);
 
-  const int32_t* btr = bt + (int64_t)s * bt_stride;
   const int64_t head_off = (int64_t)h * Gm::kTile;
   const int64_t blk_elems = (int64_t)num_kv_heads * Gm::kTile;
-  u32x4 kc[Gm::kChunks], vc[Gm::kChunks], kn[Gm::kChunks], vn[Gm::kChunks];
-  int blk = b0 + w;
-  if (blk < b1) {
-    const int64_t phys = uniform(btr[blk]);
-    load_tile<DT, D>(kp + phys * blk_elems + head_off, vp + phys * blk_elems + head_off, kc, vc,
-                     lane);
-  }
-  for (; blk < b1; blk += kWaves) {
-    const int nb = blk + kWaves;
-    if (nb < b1) {
-      const int64_t phys = uniform(btr[nb]);
-      load_tile<DT, D>(kp + phys * blk_elems + head_off, vp + phys * blk_elems + head_off, kn, vn,
-                       lane);
-    }
-    attend_block<DT, D>(st, kc, vc, blk * kBlock, n, n - 1, scale_log2, g);
-#pragma unroll
-    for (int i = 0; i < Gm::kChunks; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
+  const int nw = (b0 + w < b1) ? (b1 - b0 - w + kWaves - 1) / kWaves : 0;  // blocks of this wave
+  auto fetch = [&](TileBuf<DT, D>& tb, int i) {
+    const int64_t phys = __builtin_amdgcn_readlane(btv, i);
+    load_tile<DT, D, true>(kp + phys * blk_elems + head_off, vp + phys * blk_elems + head_off,
+                           tb.k, tb.v, lane);
+  };
+  auto consume = [&](TileBuf<DT, D>& tb, int i) {
+    attend_block<DT, D>(st, tb.k, tb.v, (b0 + w + kWaves * i) * kBlock, n, n - 1, scale_log2, g);
+  };
+  // two register buffers: the next tile is in flight while this one is used
+  TileBuf<DT, D> A, B;
+  if (nw > 0) fetch(A, 0);
+  for (int i = 0; i < nw; i += 2) {
+    if (i + 1 < nw) fetch(B, i + 1);
+    consume(A, i);
+    if (i + 1 < nw) {
+      if (i + 2 < nw) fetch(A, i + 2);
+      consume(B, i + 1);
     }
   }
 
@@ -283,31 +332,65 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
 }
 
-// Merge of decode partitions: o = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p.
-// grid (num_q_heads, num_seqs), D threads.
-template <class DT, int D>
+// Merge of decode partitions, one workgroup per (sequence, KV head):
+//   o = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// The partition weights go through LDS; every output element then sums its
+// partitions with independent loads.  Dynamic LDS: max_parts * G floats.
+template <class DT, int D, int G>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     typename DT::T* __restrict__ out, const float* __restrict__ ws_o,
     const float* __restrict__ ws_ml, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ qsl, int num_q_heads, int max_parts, int bt_stride) {
-  const int s = blockIdx.y, hh = blockIdx.x, d = threadIdx.x;
+    const int32_t* __restrict__ qsl, int num_kv_heads, int max_parts, int bt_stride) {
+  extern __shared__ float sm_w[];  // [nparts][G]
+  __shared__ float sm_M[G], sm_den[G];
+  const int s = blockIdx.x / num_kv_heads, h = blockIdx.x % num_kv_heads;
   const int qb = qsl[s];
   if (qsl[s + 1] - qb != 1) return;
   const int n = seq_lens[s];
   const int nblocks = min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks));
   const int nparts = (nblocks + kPartBlocks - 1) / kPartBlocks;
   if (nparts <= 1) return;
-  const int64_t base = (int64_t)s * max_parts * num_q_heads + hh;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ws_ml[2 * (base + (int64_t)p * num_q_heads)]);
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const int64_t idx = base + (int64_t)p * num_q_heads;
-    const float f = fast_exp2(ws_ml[2 * idx] - M) * ws_ml[2 * idx + 1];
-    num += f * ws_o[idx * D + d];
-    den += f;
+  const int hq = num_kv_heads * G;
+  const int64_t base = (int64_t)s * max_parts * hq + h * G;  // (partition 0, head h*G)
+  for (int t = threadIdx.x; t < nparts * G; t += blockDim.x) {
+    const int p = t / G, cc = t - p * G;
+    sm_w[t] = ws_ml[2 * (base + (int64_t)p * hq + cc)];
   }
-  store_elem<DT>(out, ((int64_t)qb * num_q_heads + hh) * D + d, num / den);
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float M = -INFINITY;
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, sm_w[p * G + threadIdx.x]);
+    sm_M[threadIdx.x] = M;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nparts * G; t += blockDim.x) {
+    const int p = t / G, cc = t - p * G;
+    sm_w[t] = fast_exp2(sm_w[t] - sm_M[cc]) * ws_ml[2 * (base + (int64_t)p * hq + cc) + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float den = 0.f;
+    for (int p = 0; p < nparts; ++p) den += sm_w[p * G + threadIdx.x];
+    sm_den[threadIdx.x] = den;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int cc = e / D, d = e - cc * D;
+    const float* o = ws_o + (base + cc) * D + d;
+    const int64_t step = (int64_t)hq * D;  // one partition further
+    float num = 0.f;
+    int p = 0;
+    for (; p + 4 <= nparts; p += 4) {
+      const float o0 = o[(p + 0) * step], o1 = o[(p + 1) * step];
+      const float o2 = o[(p + 2) * step], o3 = o[(p + 3) * step];
+      num += sm_w[(p + 0) * G + cc] * o0;
+      num += sm_w[(p + 1) * G + cc] * o1;
+      num += sm_w[(p + 2) * G + cc] * o2;
+      num += sm_w[(p + 3) * G + cc] * o3;
+    }
+    for (; p < nparts; ++p) num += sm_w[p * G + cc] * o[p * step];
+    store_elem<DT>(out, ((int64_t)qb * hq + h * G + cc) * D + d, num / sm_den[cc]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -411,17 +494,17 @@ struct AttnArgs {
 template <class DT, int D, int G>
 static int launch(const AttnArgs& a) {
   typedef typename DT::T T;
-  const int hq = a.num_kv_heads * G;
   dim3 blk(256);
-  dim3 gd(a.num_kv_heads * a.max_parts, a.num_seqs);
-  hipLaunchKernelGGL((decode_kernel<DT, D, G>), gd, blk, 0, a.stream, (const T*)a.q, (T*)a.out,
-                     (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride, a.seq_lens, a.qsl,
-                     a.num_kv_heads, a.scale_log2, a.max_parts, a.ws_o, a.ws_ml);
-  if (a.max_parts > 1) {
-    dim3 gm(hq, a.num_seqs);
-    hipLaunchKernelGGL((decode_merge_kernel<DT, D>), gm, dim3(D), 0, a.stream, (T*)a.out, a.ws_o,
-                       a.ws_ml, a.seq_lens, a.qsl, hq, a.max_parts, a.bt_stride);
-  }
+  const int64_t items = (int64_t)a.num_kv_heads * a.max_parts * a.num_seqs;
+  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((decode_kernel<DT, D, G>), dim3((unsigned)grid), blk, 0, a.stream,
+                     (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
+                     a.seq_lens, a.qsl, a.num_seqs, a.num_kv_heads, a.scale_log2, a.max_parts,
+                     a.ws_o, a.ws_ml);
+  if (a.max_parts > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<DT, D, G>), dim3(a.num_seqs * a.num_kv_heads), blk,
+                       (size_t)a.max_parts * G * sizeof(float), a.stream, (T*)a.out, a.ws_o,
+                       a.ws_ml, a.seq_lens, a.qsl, a.num_kv_heads, a.max_parts, a.bt_stride);
   if (a.max_q_len > 1) {
     constexpr int kTokWG = kWaves * (16 / G);
     dim3 gp(a.num_kv_heads * ((a.max_q_len + kTokWG - 1) / kTokWG), a.num_seqs);
@@ -501,8 +584,10 @@ extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void
   const int G = num_q_heads / cache->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
   if (cache->dtype == PKV_F32 && cache->head_dim == 256) return PKV_ERR_UNSUPPORTED;
-  if ((int64_t)cache->num_kv_heads * max_partitions(max_seq_len) > 0x7fffffff)
+  // decode grid (padded to whole XCD rounds) and the merge's LDS must fit their limits
+  if ((int64_t)num_seqs * cache->num_kv_heads * max_partitions(max_seq_len) + kXcds > 0x7fffffff)
     return PKV_ERR_INVALID_ARGUMENT;
+  if (max_partitions(max_seq_len) * G * (int64_t)sizeof(float) > 65536) return PKV_ERR_UNSUPPORTED;
   const size_t need = pkv_paged_attention_workspace_bytes(num_seqs, num_q_tokens, max_seq_len,
                                                           num_q_heads, cache->head_dim);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_ERR_WORKSPACE;

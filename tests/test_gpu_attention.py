@@ -41,8 +41,10 @@ def test_configs_reduced(name, kw):
     _check(workloads.scaled_spec(name, **kw), f"{name}{kw}")
 
 
-# edge lengths around a block (16) and a decode partition (512 tokens)
-EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025, 8192]
+# edge lengths around a block (16 tokens), a wavefront's share of a decode
+# partition, and the decode partition itself (1024 tokens) and its multiples
+EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 2047, 2048,
+        2049, 3073, 8192]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
