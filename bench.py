@@ -52,6 +52,28 @@ def algorithmic_bytes(spec):
     return kv, kv + qo + table
 
 
+def measured_traffic():
+    """HBM bytes per paged_attention launch from the committed counter summary,
+    or None if the kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+
+    prof = os.path.join(ROOT, "profiles", "paged_attention_decode_llama3-8b-gqa_b256_pmc.md")
+    csrc = os.path.join(ROOT, "paged_kv_cache_446_amd", "csrc")
+    try:
+        txt = open(prof).read()
+        h = hashlib.sha256()
+        for f in ("attention.hip", "pkv_device.h"):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", txt)
+    k = re.search(r"kernel_sources_sha256: ([0-9a-f]{64})", txt)
+    if not m or not k or k.group(1) != h.hexdigest():
+        return None
+    return int(m.group(1))
+
+
 def cpu_baseline(spec, out_bits, target_s):
     """The oracle (as it stands) on a bounded sample of the same workload."""
     import threadpoolctl
@@ -113,6 +135,9 @@ def main():
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (a kernel of known size for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -192,6 +217,14 @@ def main():
         if ev_b is not None:
             ev_b.record()
 
+    if args.pmc_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("pmc calibration: copied 268435456 bytes")
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -252,7 +285,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if args.config == "c3" else None,
             "algorithmic_bytes_per_launch": attn_bytes,
             "avg_launch_us": round(attn_avg * 1e3, 2),
         },
