@@ -1,5 +1,6 @@
 // PagedAttention for gfx950: decode (split-K over the paged context, then a
-// merge of the partitions) and prefill chunks (causal inside the chunk).
+// merge of the partitions) and the paged_attention entry point, which also
+// launches the prefill-chunk kernels of prefill.hip.
 //
 // The kernels find every block through the sequence's block table and read K
 // and V block by block; the result is that of attention over the same tokens
@@ -28,180 +29,16 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
-#include "pkv.h"
-#include "pkv_device.h"
+#include "attn_common.h"
 #include "pkv_host.h"
 
 namespace pkv {
 
-constexpr int kWaves = 4;        // wavefronts per workgroup
 constexpr int kPartBlocks = 64;  // blocks per decode partition (1024 tokens)
 constexpr int kPerWave = kPartBlocks / kWaves;  // blocks of a partition per wavefront
 constexpr int kXcds = 8;         // accelerator complex dies of an MI355X
 static_assert(kPerWave <= 64, "one block-table entry per lane");
 
-typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
-
-template <class DT, int D>
-struct Geo {
-  static constexpr int kChunks = D * DT::kBytes / 64;  // 16-byte operand chunks per lane per tile
-  static constexpr int kN = D / 16;                    // 16-dim slices of the output
-  static constexpr int kTile = kBlock * D;             // elements per (block, head) tile
-  static constexpr int kX = 16 / DT::kBytes;           // elements per 16-byte chunk
-};
-
-template <class DT, int D>
-struct WaveState {
-  u32x4 q[Geo<DT, D>::kChunks];  // Q^T operand of this lane's column
-  f32x4 acc[Geo<DT, D>::kN];     // O^T: lane 16g+c holds dims 16n+4g..16n+4g+3 of column c
-  float m;                       // running max of the column (log2 domain)
-  float l;                       // running sum of this lane's 4 tokens per block
-};
-
-template <class DT, int D>
-__device__ __forceinline__ void load_q(WaveState<DT, D>& st, const typename DT::T* qrow, bool valid,
-                                       int g) {
-  const u32x4* q4 = (const u32x4*)qrow;
-#pragma unroll
-  for (int kk = 0; kk < Geo<DT, D>::kChunks; ++kk)
-    st.q[kk] = valid ? q4[kk * 4 + g] : u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int n = 0; n < Geo<DT, D>::kN; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
-}
-
-// One (block, KV head) tile of K and of V into registers: chunk i*64 + lane of
-// each.  kStream marks tiles read exactly once (decode): non-temporal loads
-// keep them from displacing reusable lines in the caches.
-template <class DT, int D, bool kStream = false>
-__device__ __forceinline__ void load_tile(const typename DT::T* kt, const typename DT::T* vt,
-                                          u32x4 (&kr)[Geo<DT, D>::kChunks],
-                                          u32x4 (&vr)[Geo<DT, D>::kChunks], int lane) {
-  const u32x4* k4 = (const u32x4*)kt;
-  const u32x4* v4 = (const u32x4*)vt;
-#pragma unroll
-  for (int i = 0; i < Geo<DT, D>::kChunks; ++i) {
-    if constexpr (kStream) {
-      kr[i] = __builtin_bit_cast(u32x4, __builtin_nontemporal_load((const u32v4*)(k4 + i * kWave + lane)));
-      vr[i] = __builtin_bit_cast(u32x4, __builtin_nontemporal_load((const u32v4*)(v4 + i * kWave + lane)));
-    } else {
-      kr[i] = k4[i * kWave + lane];
-      vr[i] = v4[i * kWave + lane];
-    }
-  }
-}
-
-template <class DT, int D>
-struct TileBuf {
-  u32x4 k[Geo<DT, D>::kChunks], v[Geo<DT, D>::kChunks];
-};
-
-__device__ __forceinline__ float lanef(const u32x4& v, int e) {
-  return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
-}
-
-// One 16-token block: scores, online softmax update, P.V accumulate.
-//   tok0  absolute index of the block's first token
-//   n     tokens in the sequence (slots >= n hold stale data: never used)
-//   lim   last token this lane's column may see (inclusive, < n)
-template <class DT, int D>
-__device__ __forceinline__ void attend_block(WaveState<DT, D>& st,
-                                             const u32x4 (&kr)[Geo<DT, D>::kChunks],
-                                             u32x4 (&vr)[Geo<DT, D>::kChunks], int tok0, int n,
-                                             int lim, float scale_log2, int g) {
-  typedef Geo<DT, D> Gm;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (DT::kBytes == 2) {
-#pragma unroll
-    for (int kk = 0; kk < Gm::kChunks; ++kk) s = mma_k32(kr[kk], st.q[kk], s, DT());
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < Gm::kChunks; ++kk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s = mma_f32(lanef(kr[kk], e), lanef(st.q[kk], e), s);
-  }
-  const int t0 = tok0 + 4 * g;
-  float sv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) sv[i] = (t0 + i <= lim) ? s[i] * scale_log2 : -INFINITY;
-  float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  bm = fmaxf(bm, shfl_xor(bm, 16));
-  bm = fmaxf(bm, shfl_xor(bm, 32));
-  const float mn = fmaxf(st.m, bm);
-  const float mu = (mn == -INFINITY) ? 0.f : mn;  // a column with nothing visible yet
-  const float alpha = fast_exp2(st.m - mu);
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - mu);
-  st.m = mn;
-#pragma unroll
-  for (int nn = 0; nn < Gm::kN; ++nn) st.acc[nn] *= alpha;
-
-  // slots at or past the sequence end may hold anything (even NaN): select, never multiply
-  const bool tail = tok0 + kBlock > n;
-  if constexpr (DT::kBytes == 2) {
-    uint32_t pd0, pd1;
-    if constexpr (__is_same(DT, TBF16)) {
-      pd0 = pack2_bf16(p[0], p[1]);
-      pd1 = pack2_bf16(p[2], p[3]);
-    } else {
-      pd0 = pack2_f16(p[0], p[1]);
-      pd1 = pack2_f16(p[2], p[3]);
-    }
-    // the sum uses the rounded weights, so the output is a convex combination of V rows
-    float ps;
-    if constexpr (__is_same(DT, TBF16)) {
-      ps = (bf16_bits_to_f32(pd0 & 0xffffu) + bf16_bits_to_f32(pd0 >> 16)) +
-           (bf16_bits_to_f32(pd1 & 0xffffu) + bf16_bits_to_f32(pd1 >> 16));
-    } else {
-      ps = ((float)__builtin_bit_cast(_Float16, (uint16_t)(pd0 & 0xffffu)) +
-            (float)__builtin_bit_cast(_Float16, (uint16_t)(pd0 >> 16))) +
-           ((float)__builtin_bit_cast(_Float16, (uint16_t)(pd1 & 0xffffu)) +
-            (float)__builtin_bit_cast(_Float16, (uint16_t)(pd1 >> 16)));
-    }
-    st.l = st.l * alpha + ps;
-    if (tail) {
-      const uint32_t m0 = (t0 + 0 < n ? 0x0000ffffu : 0u) | (t0 + 1 < n ? 0xffff0000u : 0u);
-      const uint32_t m1 = (t0 + 2 < n ? 0x0000ffffu : 0u) | (t0 + 3 < n ? 0xffff0000u : 0u);
-#pragma unroll
-      for (int i = 0; i < Gm::kChunks; ++i) {
-        vr[i].x &= m0;
-        vr[i].y &= m1;
-        vr[i].z &= m0;
-        vr[i].w &= m1;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < Gm::kChunks; ++i) {
-      st.acc[2 * i] = mma_k16(vr[i].x, vr[i].y, pd0, pd1, st.acc[2 * i], DT());
-      st.acc[2 * i + 1] = mma_k16(vr[i].z, vr[i].w, pd0, pd1, st.acc[2 * i + 1], DT());
-    }
-  } else {
-    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    if (tail) {
-#pragma unroll
-      for (int i = 0; i < Gm::kChunks; ++i) {
-        vr[i].x = t0 + 0 < n ? vr[i].x : 0u;
-        vr[i].y = t0 + 1 < n ? vr[i].y : 0u;
-        vr[i].z = t0 + 2 < n ? vr[i].z : 0u;
-        vr[i].w = t0 + 3 < n ? vr[i].w : 0u;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < Gm::kChunks; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st.acc[i] = mma_f32(lanef(vr[i], j), p[j], st.acc[i]);
-  }
-}
-
-template <class DT>
-__device__ __forceinline__ void store_elem(typename DT::T* out, int64_t i, float v) {
-  if constexpr (__is_same(DT, TBF16))
-    out[i] = (uint16_t)f32_to_bf16_bits(v);
-  else
-    out[i] = (typename DT::T)v;
-}
 
 // ---------------------------------------------------------------------------
 // Decode: a 1-D grid over (sequence, partition, KV head), 4 wavefronts each.
@@ -394,102 +231,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Prefill chunks (q_len > 1): grid (num_kv_heads * q_tiles, num_seqs).  Each
-// wavefront owns 16/G query tokens x G heads and scans every block its last
-// token can see, causal inside the chunk.
-// ---------------------------------------------------------------------------
-template <class DT, int D, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(
-    const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
-    const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
-    const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ qsl, int num_kv_heads, float scale_log2) {
-  typedef Geo<DT, D> Gm;
-  constexpr int kTokW = 16 / G;            // query tokens per wavefront
-  constexpr int kTokWG = kWaves * kTokW;   // query tokens per workgroup
-  const int s = blockIdx.y;
-  const int h = blockIdx.x % num_kv_heads;
-  const int tile = blockIdx.x / num_kv_heads;
-  const int qb = qsl[s];
-  const int q_len = qsl[s + 1] - qb;
-  if (q_len <= 1) return;
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
-  const int g = lane >> 4, c = lane & 15;
-  const int wq0 = tile * kTokWG + w * kTokW;  // first query token of this wavefront
-  if (wq0 >= q_len) return;
-  const int n = seq_lens[s];
-  const int hq = num_kv_heads * G;
-  const int ctx = n - q_len;
-  const int tq = wq0 + c / G;
-  const bool valid = tq < q_len;
-  const int head = h * G + c % G;
-  if (n <= 0) {
-    if (valid)
-      for (int nn = 0; nn < Gm::kN; ++nn)
-        for (int i = 0; i < 4; ++i)
-          store_elem<DT>(out, ((int64_t)(qb + tq) * hq + head) * D + nn * 16 + 4 * g + i, 0.f);
-    return;
-  }
-  const int lim = ctx + (valid ? tq : q_len - 1);
-  WaveState<DT, D> st;
-  load_q<DT, D>(st, q + ((int64_t)(qb + (valid ? tq : 0)) * hq + head) * D, valid, g);
-
-  const int wlast = min(wq0 + kTokW, q_len) - 1;
-  const int nblk = min(max(ctx + wlast, 0) / kBlock + 1, bt_stride);
-  const int32_t* btr = bt + (int64_t)s * bt_stride;
-  const int64_t head_off = (int64_t)h * Gm::kTile;
-  const int64_t blk_elems = (int64_t)num_kv_heads * Gm::kTile;
-  u32x4 kc[Gm::kChunks], vc[Gm::kChunks], kn[Gm::kChunks], vn[Gm::kChunks];
-  {
-    const int64_t phys = uniform(btr[0]);
-    load_tile<DT, D>(kp + phys * blk_elems + head_off, vp + phys * blk_elems + head_off, kc, vc,
-                     lane);
-  }
-  for (int blk = 0; blk < nblk; ++blk) {
-    if (blk + 1 < nblk) {
-      const int64_t phys = uniform(btr[blk + 1]);
-      load_tile<DT, D>(kp + phys * blk_elems + head_off, vp + phys * blk_elems + head_off, kn, vn,
-                       lane);
-    }
-    attend_block<DT, D>(st, kc, vc, blk * kBlock, n, lim, scale_log2, g);
-#pragma unroll
-    for (int i = 0; i < Gm::kChunks; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
-    }
-  }
-  float lsum = st.l + shfl_xor(st.l, 16);
-  lsum += shfl_xor(lsum, 32);
-  const float inv = 1.f / lsum;
-  if (valid) {
-    const int64_t o = ((int64_t)(qb + tq) * hq + head) * D + 4 * g;
-#pragma unroll
-    for (int nn = 0; nn < Gm::kN; ++nn)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) store_elem<DT>(out, o + nn * 16 + i, st.acc[nn][i] * inv);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
-struct AttnArgs {
-  const void* q;
-  void* out;
-  const void* kp;
-  const void* vp;
-  const int32_t* bt;
-  int bt_stride;
-  const int32_t* seq_lens;
-  const int32_t* qsl;
-  int num_seqs, num_kv_heads, max_q_len, max_parts;
-  float scale_log2;
-  float* ws_o;
-  float* ws_ml;
-  hipStream_t stream;
-};
 
 template <class DT, int D, int G>
 static int launch(const AttnArgs& a) {
@@ -505,13 +249,6 @@ static int launch(const AttnArgs& a) {
     hipLaunchKernelGGL((decode_merge_kernel<DT, D, G>), dim3(a.num_seqs * a.num_kv_heads), blk,
                        (size_t)a.max_parts * G * sizeof(float), a.stream, (T*)a.out, a.ws_o,
                        a.ws_ml, a.seq_lens, a.qsl, a.num_kv_heads, a.max_parts, a.bt_stride);
-  if (a.max_q_len > 1) {
-    constexpr int kTokWG = kWaves * (16 / G);
-    dim3 gp(a.num_kv_heads * ((a.max_q_len + kTokWG - 1) / kTokWG), a.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<DT, D, G>), gp, blk, 0, a.stream, (const T*)a.q, (T*)a.out,
-                       (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride, a.seq_lens, a.qsl,
-                       a.num_kv_heads, a.scale_log2);
-  }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -557,8 +294,9 @@ extern "C" size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t 
     return 0;
   const int64_t parts = max_partitions(max_seq_len);
   const int64_t rows = (int64_t)num_seqs * parts * num_q_heads;
-  // (m, l) pairs, then the partition outputs, each section 256-byte aligned
-  return (size_t)(round256(rows * 2 * 4) + round256(rows * (int64_t)head_dim * 4));
+  // decode (m, l) pairs, decode partition outputs, prefill work list; each 256-byte aligned
+  return (size_t)(round256(rows * 2 * 4) + round256(rows * (int64_t)head_dim * 4) +
+                  round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads)));
 }
 
 extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void* out,
@@ -612,11 +350,18 @@ extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void
   const int64_t rows = (int64_t)num_seqs * a.max_parts * num_q_heads;
   a.ws_ml = (float*)workspace;
   a.ws_o = (float*)((char*)workspace + round256(rows * 2 * 4));
+  a.ws_pf = (char*)workspace + round256(rows * 2 * 4) + round256(rows * (int64_t)cache->head_dim * 4);
+  a.pf_items = prefill_items_bound(num_seqs, num_q_tokens, num_q_heads);
   a.stream = (hipStream_t)stream;
+  // decode rows (q_len = 1), then prefill chunks: small ones per wavefront, large ones tiled
   switch (cache->dtype) {
-    case PKV_F32: return dispatch_d<TF32>(a, cache->head_dim, G);
-    case PKV_F16: return dispatch_d<TF16>(a, cache->head_dim, G);
-    case PKV_BF16: return dispatch_d<TBF16>(a, cache->head_dim, G);
+    case PKV_F32: rc = dispatch_d<TF32>(a, cache->head_dim, G); break;
+    case PKV_F16: rc = dispatch_d<TF16>(a, cache->head_dim, G); break;
+    case PKV_BF16: rc = dispatch_d<TBF16>(a, cache->head_dim, G); break;
+    default: return PKV_ERR_UNSUPPORTED;
   }
-  return PKV_ERR_UNSUPPORTED;
+  if (rc != PKV_OK || max_q_len <= 1) return rc;
+  rc = launch_prefill_small(a, cache->dtype, cache->head_dim, G);
+  if (rc != PKV_OK || (int64_t)max_q_len * G <= kSmallChunkCols) return rc;
+  return launch_prefill_tiled(a, cache->dtype, cache->head_dim, G);
 }

@@ -1,0 +1,212 @@
+// Device building blocks shared by the attention kernels of libpkv (decode and
+// prefill): tile geometry, the per-wavefront online-softmax state, tile loads
+// and the 16-token block step.  Tile layouts are those of include/pkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pkv.h"
+#include "pkv_device.h"
+
+namespace pkv {
+
+constexpr int kWaves = 4;  // wavefronts per decode workgroup
+
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+
+template <class DT, int D>
+struct Geo {
+  static constexpr int kChunks = D * DT::kBytes / 64;  // 16-byte operand chunks per lane per tile
+  static constexpr int kN = D / 16;                    // 16-dim slices of the output
+  static constexpr int kTile = kBlock * D;             // elements per (block, head) tile
+  static constexpr int kX = 16 / DT::kBytes;           // elements per 16-byte chunk
+};
+
+template <class DT, int D>
+struct WaveState {
+  u32x4 q[Geo<DT, D>::kChunks];  // Q^T operand of this lane's column
+  f32x4 acc[Geo<DT, D>::kN];     // O^T: lane 16g+c holds dims 16n+4g..16n+4g+3 of column c
+  float m;                       // running max of the column (log2 domain)
+  float l;                       // running sum of this lane's 4 tokens per block
+};
+
+template <class DT, int D>
+__device__ __forceinline__ void load_q(WaveState<DT, D>& st, const typename DT::T* qrow, bool valid,
+                                       int g) {
+  const u32x4* q4 = (const u32x4*)qrow;
+#pragma unroll
+  for (int kk = 0; kk < Geo<DT, D>::kChunks; ++kk)
+    st.q[kk] = valid ? q4[kk * 4 + g] : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int n = 0; n < Geo<DT, D>::kN; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// One (block, KV head) tile of K and of V into registers: chunk i*64 + lane of
+// each.  kStream marks tiles read exactly once (decode): non-temporal loads
+// keep them from displacing reusable lines in the caches.
+template <class DT, int D, bool kStream = false>
+__device__ __forceinline__ void load_tile(const typename DT::T* kt, const typename DT::T* vt,
+                                          u32x4 (&kr)[Geo<DT, D>::kChunks],
+                                          u32x4 (&vr)[Geo<DT, D>::kChunks], int lane) {
+  const u32x4* k4 = (const u32x4*)kt;
+  const u32x4* v4 = (const u32x4*)vt;
+#pragma unroll
+  for (int i = 0; i < Geo<DT, D>::kChunks; ++i) {
+    if constexpr (kStream) {
+      kr[i] = __builtin_bit_cast(u32x4, __builtin_nontemporal_load((const u32v4*)(k4 + i * kWave + lane)));
+      vr[i] = __builtin_bit_cast(u32x4, __builtin_nontemporal_load((const u32v4*)(v4 + i * kWave + lane)));
+    } else {
+      kr[i] = k4[i * kWave + lane];
+      vr[i] = v4[i * kWave + lane];
+    }
+  }
+}
+
+template <class DT, int D>
+struct TileBuf {
+  u32x4 k[Geo<DT, D>::kChunks], v[Geo<DT, D>::kChunks];
+};
+
+__device__ __forceinline__ float lanef(const u32x4& v, int e) {
+  return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+}
+
+// One 16-token block: scores, online softmax update, P.V accumulate.
+//   tok0  absolute index of the block's first token
+//   n     tokens in the sequence (slots >= n hold stale data: never used)
+//   lim   last token this lane's column may see (inclusive, < n)
+template <class DT, int D>
+__device__ __forceinline__ void attend_block(WaveState<DT, D>& st,
+                                             const u32x4 (&kr)[Geo<DT, D>::kChunks],
+                                             u32x4 (&vr)[Geo<DT, D>::kChunks], int tok0, int n,
+                                             int lim, float scale_log2, int g) {
+  typedef Geo<DT, D> Gm;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (DT::kBytes == 2) {
+#pragma unroll
+    for (int kk = 0; kk < Gm::kChunks; ++kk) s = mma_k32(kr[kk], st.q[kk], s, DT());
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < Gm::kChunks; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mma_f32(lanef(kr[kk], e), lanef(st.q[kk], e), s);
+  }
+  const int t0 = tok0 + 4 * g;
+  float sv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sv[i] = (t0 + i <= lim) ? s[i] * scale_log2 : -INFINITY;
+  float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  bm = fmaxf(bm, shfl_xor(bm, 16));
+  bm = fmaxf(bm, shfl_xor(bm, 32));
+  const float mn = fmaxf(st.m, bm);
+  const float mu = (mn == -INFINITY) ? 0.f : mn;  // a column with nothing visible yet
+  const float alpha = fast_exp2(st.m - mu);
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - mu);
+  st.m = mn;
+#pragma unroll
+  for (int nn = 0; nn < Gm::kN; ++nn) st.acc[nn] *= alpha;
+
+  // slots at or past the sequence end may hold anything (even NaN): select, never multiply
+  const bool tail = tok0 + kBlock > n;
+  if constexpr (DT::kBytes == 2) {
+    uint32_t pd0, pd1;
+    if constexpr (__is_same(DT, TBF16)) {
+      pd0 = pack2_bf16(p[0], p[1]);
+      pd1 = pack2_bf16(p[2], p[3]);
+    } else {
+      pd0 = pack2_f16(p[0], p[1]);
+      pd1 = pack2_f16(p[2], p[3]);
+    }
+    // the sum uses the rounded weights, so the output is a convex combination of V rows
+    float ps;
+    if constexpr (__is_same(DT, TBF16)) {
+      ps = (bf16_bits_to_f32(pd0 & 0xffffu) + bf16_bits_to_f32(pd0 >> 16)) +
+           (bf16_bits_to_f32(pd1 & 0xffffu) + bf16_bits_to_f32(pd1 >> 16));
+    } else {
+      ps = ((float)__builtin_bit_cast(_Float16, (uint16_t)(pd0 & 0xffffu)) +
+            (float)__builtin_bit_cast(_Float16, (uint16_t)(pd0 >> 16))) +
+           ((float)__builtin_bit_cast(_Float16, (uint16_t)(pd1 & 0xffffu)) +
+            (float)__builtin_bit_cast(_Float16, (uint16_t)(pd1 >> 16)));
+    }
+    st.l = st.l * alpha + ps;
+    if (tail) {
+      const uint32_t m0 = (t0 + 0 < n ? 0x0000ffffu : 0u) | (t0 + 1 < n ? 0xffff0000u : 0u);
+      const uint32_t m1 = (t0 + 2 < n ? 0x0000ffffu : 0u) | (t0 + 3 < n ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int i = 0; i < Gm::kChunks; ++i) {
+        vr[i].x &= m0;
+        vr[i].y &= m1;
+        vr[i].z &= m0;
+        vr[i].w &= m1;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Gm::kChunks; ++i) {
+      st.acc[2 * i] = mma_k16(vr[i].x, vr[i].y, pd0, pd1, st.acc[2 * i], DT());
+      st.acc[2 * i + 1] = mma_k16(vr[i].z, vr[i].w, pd0, pd1, st.acc[2 * i + 1], DT());
+    }
+  } else {
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < Gm::kChunks; ++i) {
+        vr[i].x = t0 + 0 < n ? vr[i].x : 0u;
+        vr[i].y = t0 + 1 < n ? vr[i].y : 0u;
+        vr[i].z = t0 + 2 < n ? vr[i].z : 0u;
+        vr[i].w = t0 + 3 < n ? vr[i].w : 0u;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Gm::kChunks; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.acc[i] = mma_f32(lanef(vr[i], j), p[j], st.acc[i]);
+  }
+}
+
+template <class DT>
+__device__ __forceinline__ void store_elem(typename DT::T* out, int64_t i, float v) {
+  if constexpr (__is_same(DT, TBF16))
+    out[i] = (uint16_t)f32_to_bf16_bits(v);
+  else
+    out[i] = (typename DT::T)v;
+}
+
+// Arguments of one paged_attention call, as the kernels' launchers see them.
+struct AttnArgs {
+  const void* q;
+  void* out;
+  const void* kp;
+  const void* vp;
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int num_seqs, num_kv_heads, max_q_len, max_parts;
+  float scale_log2;
+  float* ws_o;
+  float* ws_ml;
+  void* ws_pf;        // tiled-prefill work list (pf_items entries) and its queue counters
+  int64_t pf_items;
+  hipStream_t stream;
+};
+
+// Launchers of the prefill kernels (prefill.hip).  Each returns PKV_OK or a
+// PKV_ERR_* status; both only enqueue work on a.stream.
+//   small chunks (q_len * G <= 64 columns): one wavefront per 16 columns
+//   large chunks: planned work list + LDS-tiled persistent kernel
+int launch_prefill_small(const AttnArgs& a, int dtype, int head_dim, int G);
+int launch_prefill_tiled(const AttnArgs& a, int dtype, int head_dim, int G);
+// Bound on the tiled prefill's work items, and the workspace bytes they and the
+// queue counters take.
+int64_t prefill_items_bound(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads);
+int64_t prefill_workspace_bytes(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads);
+// Columns (query token, head pairs) at or below which a chunk takes the small kernel.
+constexpr int kSmallChunkCols = 64;
+
+}  // namespace pkv

@@ -137,3 +137,34 @@ def test_shared_prefix_equals_private_copies_bitwise():
     torch.cuda.synchronize()
     assert np.array_equal(gp.host_bits(out, "bf16"), rs.out_bits())
     assert len(rs.flow.step.pairs) == 3  # even sequences copied the last shared block
+
+
+# Large chunks take the LDS-tiled prefill kernel (more than 64 (token, head)
+# columns): several query tiles per chunk, contexts of zero, one block, odd
+# block counts and past a partition, next to decode rows and small chunks.
+@pytest.mark.parametrize("dtype,hq,hkv,d", [
+    ("bf16", 32, 8, 128), ("f16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 16, 8, 64),
+    ("f16", 16, 2, 256), ("bf16", 64, 8, 128), ("bf16", 8, 4, 64),
+])
+def test_prefill_tiled_chunks(dtype, hq, hkv, d):
+    ctx = np.array([0, 16, 33, 700, 1500, 3000, 0, 90], dtype=np.int64)
+    q = np.array([300, 130, 77, 64, 513, 40, 1, 17], dtype=np.int64)
+    spec = workloads.make_spec(f"pf-{hq}-{hkv}-{d}", (446, 97, hq, hkv, d), dtype, hq, hkv, d, ctx, q)
+    _check(spec, f"tiled prefill {dtype} {hq}/{hkv} d{d}")
+
+
+def test_prefill_tiled_deterministic_and_placement_invariant():
+    import torch
+
+    gp = _gp()
+    ctx = np.array([500, 0, 2000], dtype=np.int64)
+    q = np.array([200, 96, 33], dtype=np.int64)
+    spec = workloads.make_spec("pf-det", (446, 98), "bf16", 32, 8, 128, ctx, q)
+    a = gp.prepare(spec)
+    first = a.out_bits().copy()
+    gp.attention(a)
+    torch.cuda.synchronize()
+    assert np.array_equal(first, a.out_bits())
+    other = np.random.default_rng(78).permutation(spec.num_blocks).astype(np.int32)
+    b = gp.prepare(spec, free_order=other)
+    assert np.array_equal(first, b.out_bits())
