@@ -104,17 +104,26 @@ __global__ __launch_bounds__(256) void prefill_small_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfBuckets = 64;  // context-length classes of the plan (1024 tokens each)
+constexpr int kPfBuckets = 64;     // context-length classes of the plan (1024 tokens each)
+constexpr int kPfDepth = 2;        // steps of K/V in flight per thread (register stages)
+constexpr int kPfTableMax = 8192;  // block-table entries an item keeps in LDS (131072 tokens)
+// The exponentials use a reference max that may lag the true running max by
+// up to 2^kPfLag (weights <= 2^8, far from overflow); the accumulators are
+// rescaled only when some column's max moves further than that.
+constexpr float kPfLag = 8.f;
 
 template <class DT, int D>
 struct PfGeo {
   static constexpr int kCT = D <= 128 ? 2 : 1;                      // 16-column tiles per wave
+  static constexpr int kSB = D <= 128 ? 4 : 2;                      // KV blocks per pipeline step
   static constexpr int kCols = kPfWaves * kCT * 16;                 // columns per item
   static constexpr int kTileChunks = kBlock * D * DT::kBytes / 16;  // 16-byte chunks per tile
-  static constexpr int kStageChunks = 4 * kTileChunks;              // K, V of two blocks
+  static constexpr int kStageChunks = 2 * kSB * kTileChunks;        // K and V of a step
   static constexpr int kPerThread = kStageChunks / kPfThreads;
   static constexpr int kLdsBytes = 2 * kStageChunks * 16;           // double buffer
   static_assert(kStageChunks % kPfThreads == 0, "whole chunks per thread");
+  static_assert(kSB % 2 == 0 && kPfTableMax % kSB == 0, "whole block pairs per step");
+  static_assert(kLdsBytes + kPfTableMax * 4 + 64 <= 160 * 1024, "LDS of one workgroup");
 };
 
 struct PfItem {
@@ -182,6 +191,16 @@ __device__ __forceinline__ void store4(typename DT::T* out, int64_t i, f32x4 v) 
   }
 }
 
+// max over the four lanes c, c+16, c+32, c+48 of a column (row swaps, no LDS)
+__device__ __forceinline__ float col_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <class DT, int D, int G>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
@@ -194,9 +213,15 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
   typedef Geo<DT, D> Gm;
   typedef PfGeo<DT, D> P;
   constexpr int kCT = P::kCT;
+  constexpr int kSB = P::kSB;
+  constexpr int kTC = P::kTileChunks;
   constexpr int QT = P::kCols / G;  // query tokens per item
-  extern __shared__ u32x4 sm_stage[];  // [2][K0, V0, K1, V1][kTileChunks]
+  // LDS stage: [K of blocks 0..kSB-1][V of block pair 0: slices r=0][r=1][pair 1: r=0][r=1]...
+  // A V entry of 16 bytes holds the 8-byte half r of one chunk for the pair's first block,
+  // then for its second: exactly one A operand of the 32-token V^T.P^T product.
+  extern __shared__ u32x4 sm_stage[];
   __shared__ int sm_item;
+  __shared__ int32_t sm_bt[kPfTableMax];  // the item's block-table entries (one segment)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
@@ -221,7 +246,8 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
     // this wavefront's columns: col = (w*kCT + ct)*16 + c -> token tq0 + col/G, head h*G + col%G
     u32x4 qv[kCT][Gm::kChunks];
     f32x4 acc[kCT][Gm::kN];
-    float m[kCT], l[kCT];
+    f32x4 accl[kCT];  // row sums of the rounded weights (every element holds the column's sum)
+    float m[kCT];     // reference max of each column (log2 domain)
     int lim[kCT];
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
@@ -235,30 +261,42 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
       for (int kk = 0; kk < Gm::kChunks; ++kk) qv[ct][kk] = valid ? q4[kk * 4 + g] : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int nn = 0; nn < Gm::kN; ++nn) acc[ct][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accl[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       m[ct] = -INFINITY;
-      l[ct] = 0.f;
     }
     const int wave_tq = tq0 + (w * kCT * 16) / G;  // first token of this wavefront
     const bool wave_active = wave_tq < tq_end;
     const int wave_min_lim = ctx + wave_tq;
     // blocks the tile's last row can see (a sequence with no tokens sees none)
     const int nvis = n > 0 ? min((ctx + tq_end - 1) / kBlock + 1, bt_stride) : 0;
-    const int steps = (nvis + 1) / 2;
+    int seg0 = 0;  // first block of the block-table segment held in sm_bt
 
-    u32x4 stg[P::kPerThread];
-    auto fetch_stage = [&](int j) {
+    // K/V of step j: registers -> LDS buffer j & 1; the next kPfDepth-1 steps are in flight.
+    // Thread chunk k of a step is chunk ci of tile t = 2b + (0 for K, 1 for V) of the step's
+    // block b.  Loads are unconditional (blocks past the visible range re-read the last one)
+    // so that each wait covers exactly one step; masking happens when the step is stored.
+    u32x4 stg[kPfDepth][P::kPerThread];
+    auto fetch_stage = [&](u32x4 (&dst)[P::kPerThread], int j) {
 #pragma unroll
       for (int k = 0; k < P::kPerThread; ++k) {
         const int idx = tid + k * kPfThreads;
-        const int t = idx / P::kTileChunks, ci = idx % P::kTileChunks;
-        const int blk = 2 * j + (t >> 1);
-        const bool is_v = t & 1;
-        u32x4 v = {0, 0, 0, 0};
-        if (blk < nvis) {
-          const int64_t phys = btr[blk];
-          const u32x4* src = (const u32x4*)((is_v ? vp : kp) + phys * blk_elems + head_off);
-          v = src[ci];
-          if (is_v && blk * kBlock + kBlock > n) {
+        const int t = idx / kTC, ci = idx % kTC;
+        const int blk = min(kSB * j + (t >> 1), nvis - 1);
+        const int64_t phys = sm_bt[blk - seg0];
+        const u32x4* src = (const u32x4*)(((t & 1) ? vp : kp) + phys * blk_elems + head_off);
+        dst[k] = src[ci];
+      }
+    };
+    auto store_stage = [&](const u32x4 (&src)[P::kPerThread], int j, int buf) {
+      u32x4* st = sm_stage + buf * P::kStageChunks;
+#pragma unroll
+      for (int k = 0; k < P::kPerThread; ++k) {
+        const int idx = tid + k * kPfThreads;
+        const int t = idx / kTC, ci = idx % kTC;
+        const int b = t >> 1, blk = kSB * j + b;
+        u32x4 v = blk < nvis ? src[k] : u32x4{0, 0, 0, 0};
+        if (t & 1) {
+          if (blk * kBlock + kBlock > n) {
             // V of slots past the sequence end may be anything: zero it (tokens 4g'..4g'+3)
             const int t0 = blk * kBlock + 4 * ((ci >> 4) & 3);
             const uint32_t m0 = (t0 + 0 < n ? 0x0000ffffu : 0u) | (t0 + 1 < n ? 0xffff0000u : 0u);
@@ -268,102 +306,134 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
             v.z &= m0;
             v.w &= m1;
           }
+          uint2* v2 = (uint2*)(st + (kSB + 2 * (b >> 1)) * kTC);
+          v2[2 * ci + (b & 1)] = uint2{v.x, v.y};
+          v2[2 * (kTC + ci) + (b & 1)] = uint2{v.z, v.w};
+        } else {
+          st[b * kTC + ci] = v;
         }
-        stg[k] = v;
       }
-    };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-      for (int k = 0; k < P::kPerThread; ++k) sm_stage[buf * P::kStageChunks + tid + k * kPfThreads] = stg[k];
     };
     auto compute = [&](int j, int buf) {
       const u32x4* st = sm_stage + buf * P::kStageChunks;
-      const int t0 = 32 * j;
-      const bool need_mask = t0 + 31 > wave_min_lim;
-      f32x4 sc[2][kCT];
+      const int t0 = kSB * kBlock * j;
+      const bool need_mask = t0 + kSB * kBlock - 1 > wave_min_lim;
+      // S^T = K.Q^T: lane 16g+c holds tokens 4g..4g+3 of each block for column c
+      f32x4 sc[kSB][kCT];
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
+      for (int b = 0; b < kSB; ++b) {
         u32x4 kr[Gm::kChunks];
 #pragma unroll
-        for (int kk = 0; kk < Gm::kChunks; ++kk) kr[kk] = st[(2 * bb) * P::kTileChunks + kk * kWave + lane];
+        for (int kk = 0; kk < Gm::kChunks; ++kk) kr[kk] = st[b * kTC + kk * kWave + lane];
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct) {
-          f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < Gm::kChunks; ++kk) acc_s = mma_k32(kr[kk], qv[ct][kk], acc_s, DT());
-          sc[bb][ct] = acc_s;
+          for (int kk = 0; kk < Gm::kChunks; ++kk) a = mma_k32(kr[kk], qv[ct][kk], a, DT());
+          sc[b][ct] = a;
         }
       }
-      u32x4 pk[kCT];
+      // column maxima of this step; the reference max moves only when one of them exceeds it
+      // by more than kPfLag (a wave-wide decision)
+      float bms[kCT];
+      bool move = false;
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = sc[0][ct][i];
-          v[4 + i] = sc[1][ct][i];
-        }
         if (need_mask) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int t = t0 + (i >> 2) * 16 + 4 * g + (i & 3);
-            v[i] = t <= lim[ct] ? v[i] : -INFINITY;
-          }
-        }
-        float bm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                         fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-        bm = fmaxf(bm, shfl_xor(bm, 16));
-        bm = fmaxf(bm, shfl_xor(bm, 32));
-        const float mn = fmaxf(m[ct], bm * scale_log2);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;  // a column with nothing visible yet
-        const float alpha = fast_exp2(m[ct] - mu);
-        float p[8];
+          for (int b = 0; b < kSB; ++b)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(v[i], scale_log2, -mu));
-        l[ct] = l[ct] * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-        m[ct] = mn;
-#pragma unroll
-        for (int nn = 0; nn < Gm::kN; ++nn) acc[ct][nn] *= alpha;
-        if constexpr (__is_same(DT, TBF16)) {
-          pk[ct] = u32x4{pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]),
-                         pack2_bf16(p[6], p[7])};
-        } else {
-          pk[ct] = u32x4{pack2_f16(p[0], p[1]), pack2_f16(p[2], p[3]), pack2_f16(p[4], p[5]),
-                         pack2_f16(p[6], p[7])};
+            for (int i = 0; i < 4; ++i) {
+              const int t = t0 + b * kBlock + 4 * g + i;
+              sc[b][ct][i] = t <= lim[ct] ? sc[b][ct][i] : -INFINITY;
+            }
         }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < kSB; ++b)
+          bm = fmaxf(bm, fmaxf(fmaxf(sc[b][ct][0], sc[b][ct][1]), fmaxf(sc[b][ct][2], sc[b][ct][3])));
+        bms[ct] = col_max4(bm) * scale_log2;
+        move |= bms[ct] > m[ct] + kPfLag;  // also the first visible key of a column (m = -inf)
       }
-#pragma unroll
-      for (int mm = 0; mm < Gm::kChunks; ++mm) {
-        const u32x4 v0 = st[1 * P::kTileChunks + mm * kWave + lane];
-        const u32x4 v1 = st[3 * P::kTileChunks + mm * kWave + lane];
-        const u32x4 lo = {v0.x, v0.y, v1.x, v1.y};  // dims of slice 2mm: tokens 4g.. of both blocks
-        const u32x4 hi = {v0.z, v0.w, v1.z, v1.w};  // slice 2mm+1
+      if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct) {
-          acc[ct][2 * mm] = mma_k32(lo, pk[ct], acc[ct][2 * mm], DT());
-          acc[ct][2 * mm + 1] = mma_k32(hi, pk[ct], acc[ct][2 * mm + 1], DT());
+          const float mn = fmaxf(m[ct], bms[ct]);
+          const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[ct] - mn);
+#pragma unroll
+          for (int nn = 0; nn < Gm::kN; ++nn) acc[ct][nn] *= alpha;
+          accl[ct] *= alpha;
+          m[ct] = mn;
         }
+      }
+      const uint32_t one2 = __is_same(DT, TBF16) ? 0x3F803F80u : 0x3C003C00u;
+      const u32x4 ones = {one2, one2, one2, one2};
+#pragma unroll
+      for (int pp = 0; pp < kSB / 2; ++pp) {
+        // weights of the block pair: lane 16g+c holds tokens 4g..4g+3 of both blocks (k = 8g..)
+        u32x4 pk[kCT];
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) {
+          const float mu = m[ct] == -INFINITY ? 0.f : m[ct];  // nothing visible yet
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(fmaf(sc[2 * pp][ct][i], scale_log2, -mu));
+            p[4 + i] = fast_exp2(fmaf(sc[2 * pp + 1][ct][i], scale_log2, -mu));
+          }
+          if constexpr (__is_same(DT, TBF16)) {
+            pk[ct] = u32x4{pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]),
+                           pack2_bf16(p[6], p[7])};
+          } else {
+            pk[ct] = u32x4{pack2_f16(p[0], p[1]), pack2_f16(p[2], p[3]), pack2_f16(p[4], p[5]),
+                           pack2_f16(p[6], p[7])};
+          }
+        }
+        // O^T += V^T . P^T over the pair's 32 tokens, and the row sums against a slice of ones
+#pragma unroll
+        for (int mm = 0; mm < Gm::kChunks; ++mm) {
+          const u32x4 lo = st[(kSB + 2 * pp) * kTC + mm * kWave + lane];      // dim slice 2mm
+          const u32x4 hi = st[(kSB + 2 * pp + 1) * kTC + mm * kWave + lane];  // slice 2mm+1
+#pragma unroll
+          for (int ct = 0; ct < kCT; ++ct) {
+            acc[ct][2 * mm] = mma_k32(lo, pk[ct], acc[ct][2 * mm], DT());
+            acc[ct][2 * mm + 1] = mma_k32(hi, pk[ct], acc[ct][2 * mm + 1], DT());
+          }
+        }
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) accl[ct] = mma_k32(ones, pk[ct], accl[ct], DT());
       }
     };
 
-    if (steps > 0) {
-      fetch_stage(0);
-      store_stage(0);
+    // the block table goes through LDS in segments of kPfTableMax blocks; steps j in [js, je)
+    for (; seg0 < nvis; seg0 += kPfTableMax) {
+      const int seg_n = min(kPfTableMax, nvis - seg0);
+      for (int i = tid; i < seg_n; i += kPfThreads) sm_bt[i] = btr[seg0 + i];
       __syncthreads();
-      for (int j = 0; j < steps; ++j) {
-        if (j + 1 < steps) fetch_stage(j + 1);
-        if (wave_active) compute(j, j & 1);
-        if (j + 1 < steps) store_stage((j + 1) & 1);
-        __syncthreads();
+      const int js = seg0 / kSB, je = (seg0 + seg_n + kSB - 1) / kSB;
+      const int jl = je - 1;  // steps past the segment fetch its last step again (unused)
+#pragma unroll
+      for (int u = 0; u + 1 < kPfDepth; ++u) fetch_stage(stg[u], min(js + u, jl));
+      store_stage(stg[0], js, js & 1);
+      __syncthreads();
+      for (int j0 = js; j0 < je; j0 += kPfDepth) {
+#pragma unroll
+        for (int u = 0; u < kPfDepth; ++u) {
+          const int j = j0 + u;  // K/V of step j: stg[u] and LDS buffer j & 1
+          if (j >= je) break;
+          fetch_stage(stg[(u + kPfDepth - 1) % kPfDepth], min(j + kPfDepth - 1, jl));
+          if (wave_active) compute(j, j & 1);
+          if (j + 1 < je) store_stage(stg[(u + 1) % kPfDepth], j + 1, (j + 1) & 1);
+          __syncthreads();
+        }
       }
     }
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
-      float lsum = l[ct] + shfl_xor(l[ct], 16);
-      lsum += shfl_xor(lsum, 32);
+      const float lsum = accl[ct][0];
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // nothing visible -> zeros
-      if (lim[ct] >= 0 || (n <= 0 && tq0 + ((w * kCT + ct) * 16 + c) / G < tq_end)) {
-        const int col = (w * kCT + ct) * 16 + c;
+      const int col = (w * kCT + ct) * 16 + c;
+      if (tq0 + col / G < tq_end && (lim[ct] >= 0 || n <= 0)) {
         const int64_t o = ((int64_t)(qb + tq0 + col / G) * hq + h * G + col % G) * D + 4 * g;
 #pragma unroll
         for (int nn = 0; nn < Gm::kN; ++nn) store4<DT>(out, o + nn * 16, acc[ct][nn] * inv);
