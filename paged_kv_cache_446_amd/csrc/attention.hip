@@ -52,11 +52,90 @@ constexpr int decode_occupancy() {
   return (DT::kBytes == 2 && D <= 128) ? 3 : 1;
 }
 
-// Workgroup id -> work item.  Dispatch deals consecutive ids round-robin over
-// the XCDs; item j = (id % 8) * (grid / 8) + id / 8 gives every XCD one
-// contiguous run of items (the host pads the grid to a multiple of 8).
-__device__ __forceinline__ int xcd_item(int id, int grid) {
-  return (id % kXcds) * (grid / kXcds) + id / kXcds;
+// Work lists of one call, written by decode_plan_kernel: the live decode items
+// (sequence, partition) in sequence order, and the sequences whose partitions
+// need merging.  plan[0] = number of items, plan[1] = number of merges.
+struct DecodePlan {
+  int32_t* counts;
+  int2* items;     // [num_seqs * max_parts]
+  int32_t* merge;  // [num_seqs]
+};
+
+// One workgroup of 1024 threads; thread t owns sequences [t*k, t*k + k).
+// A decode row (q_len = 1) of a sequence with n > 0 tokens has one item per
+// 1024-token partition; an empty sequence has one item (its zero output).
+__global__ __launch_bounds__(1024) void decode_plan_kernel(
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int num_seqs,
+    int bt_stride, int max_parts, int32_t* __restrict__ counts, int2* __restrict__ items,
+    int32_t* __restrict__ merge) {
+  __shared__ int sm_tot[2][1024 / kWave];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int k = (num_seqs + blockDim.x - 1) / blockDim.x;
+  const int s0 = tid * k;
+  int nit = 0, nmg = 0;
+  for (int j = 0; j < k; ++j) {
+    const int s = s0 + j;
+    if (s >= num_seqs) break;
+    if (qsl[s + 1] - qsl[s] != 1) continue;
+    const int n = seq_lens[s];
+    const int nb = n > 0 ? min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks)) : 0;
+    const int np = n > 0 ? (nb + kPartBlocks - 1) / kPartBlocks : 1;
+    nit += np;
+    nmg += np > 1;
+  }
+  // exclusive prefix of (nit, nmg) over the workgroup: wave scan, then wave totals
+  int xi = nit, xm = nmg;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int yi = __shfl_up(xi, off), ym = __shfl_up(xm, off);
+    if (lane >= off) {
+      xi += yi;
+      xm += ym;
+    }
+  }
+  if (lane == kWave - 1) {
+    sm_tot[0][w] = xi;
+    sm_tot[1][w] = xm;
+  }
+  __syncthreads();
+  int bi = 0, bm = 0, ti = 0, tm = 0;
+  for (int ww = 0; ww < (int)(blockDim.x / kWave); ++ww) {
+    if (ww < w) {
+      bi += sm_tot[0][ww];
+      bm += sm_tot[1][ww];
+    }
+    ti += sm_tot[0][ww];
+    tm += sm_tot[1][ww];
+  }
+  int pi = bi + xi - nit, pm = bm + xm - nmg;
+  for (int j = 0; j < k; ++j) {
+    const int s = s0 + j;
+    if (s >= num_seqs) break;
+    if (qsl[s + 1] - qsl[s] != 1) continue;
+    const int n = seq_lens[s];
+    const int nb = n > 0 ? min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks)) : 0;
+    const int np = n > 0 ? (nb + kPartBlocks - 1) / kPartBlocks : 1;
+    for (int p = 0; p < np; ++p) items[pi + p] = int2{s, p};
+    pi += np;
+    if (np > 1) merge[pm++] = s;
+  }
+  if (tid == 0) {
+    counts[0] = ti;
+    counts[1] = tm;
+  }
+}
+
+// Workgroup id -> index into a list of `live` work units.  Dispatch deals
+// consecutive ids round-robin over the XCDs; unit j = (id % 8) * C + id / 8
+// with C = ceil(live / 8) gives every XCD one contiguous run of units.  Ids
+// whose unit is past the list (the grid is sized for the worst case) come
+// last in dispatch order and return at once; returns -1 for them.
+__device__ __forceinline__ int xcd_unit(int id, int live) {
+  const int per = (live + kXcds - 1) / kXcds;
+  const int r = id / kXcds;
+  if (r >= per) return -1;
+  const int j = (id % kXcds) * per + r;
+  return j < live ? j : -1;
 }
 
 template <class DT, int D, int G>
@@ -65,15 +144,14 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
                    const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
                    const int32_t* __restrict__ bt, int bt_stride,
                    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
-                   int num_seqs, int num_kv_heads, float scale_log2, int max_parts,
-                   float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+                   int num_kv_heads, float scale_log2, int max_parts,
+                   float* __restrict__ ws_o, float* __restrict__ ws_ml, DecodePlan plan) {
   typedef Geo<DT, D> Gm;
-  const int j = xcd_item(blockIdx.x, gridDim.x);
+  const int j = xcd_unit(blockIdx.x, plan.counts[0] * num_kv_heads);
+  if (j < 0) return;
   const int h = j % num_kv_heads;
-  const int sp = j / num_kv_heads;
-  const int part = sp % max_parts;
-  const int s = sp / max_parts;
-  if (s >= num_seqs) return;  // grid padding
+  const int2 item = plan.items[j / num_kv_heads];
+  const int s = item.x, part = item.y;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int b0 = part * kPartBlocks;
@@ -116,17 +194,27 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
   auto consume = [&](TileBuf<DT, D>& tb, int i) {
     attend_block<DT, D>(st, tb.k, tb.v, (b0 + w + kWaves * i) * kBlock, n, n - 1, scale_log2, g);
   };
-  // two register buffers: the next tile is in flight while this one is used
+  // two register buffers, both in flight: each iteration uses a tile and refills its buffer
+  // two tiles ahead.  The prologue waits once for Q and the first two tiles; after that
+  // every wait covers exactly the tile about to be used, and the refill is kept after the
+  // use (a hoisted load would need fresh registers and a copy at the loop edge).
   TileBuf<DT, D> A, B;
   if (nw > 0) fetch(A, 0);
-  for (int i = 0; i < nw; i += 2) {
-    if (i + 1 < nw) fetch(B, i + 1);
+  if (nw > 1) fetch(B, 1);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+  int i = 0;
+  for (; i + 3 < nw; i += 2) {
     consume(A, i);
-    if (i + 1 < nw) {
-      if (i + 2 < nw) fetch(A, i + 2);
-      consume(B, i + 1);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(A, i + 2);
+    consume(B, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(B, i + 3);
   }
+  if (i < nw) consume(A, i);
+  if (i + 2 < nw) fetch(A, i + 2);
+  if (i + 1 < nw) consume(B, i + 1);
+  if (i + 2 < nw) consume(A, i + 2);
 
   // merge the four wavefronts through LDS
   __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
@@ -171,16 +259,20 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
 
 // Merge of decode partitions, one workgroup per (sequence, KV head):
 //   o = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-// The partition weights go through LDS; every output element then sums its
-// partitions with independent loads.  Dynamic LDS: max_parts * G floats.
+// Every thread owns outputs of one query head and loads the (m, l, o) of all
+// partitions at once, kMergeBatch partitions per round, so a merge costs one
+// memory round trip after the sequence metadata (C3-like contexts: one round).
+constexpr int kMergeBatch = 8;
+
 template <class DT, int D, int G>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     typename DT::T* __restrict__ out, const float* __restrict__ ws_o,
     const float* __restrict__ ws_ml, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ qsl, int num_kv_heads, int max_parts, int bt_stride) {
-  extern __shared__ float sm_w[];  // [nparts][G]
-  __shared__ float sm_M[G], sm_den[G];
-  const int s = blockIdx.x / num_kv_heads, h = blockIdx.x % num_kv_heads;
+    const int32_t* __restrict__ qsl, int num_kv_heads, int max_parts, int bt_stride,
+    DecodePlan plan) {
+  const int j = xcd_unit(blockIdx.x, plan.counts[1] * num_kv_heads);
+  if (j < 0) return;
+  const int s = plan.merge[j / num_kv_heads], h = j % num_kv_heads;
   const int qb = qsl[s];
   if (qsl[s + 1] - qb != 1) return;
   const int n = seq_lens[s];
@@ -189,44 +281,35 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (nparts <= 1) return;
   const int hq = num_kv_heads * G;
   const int64_t base = (int64_t)s * max_parts * hq + h * G;  // (partition 0, head h*G)
-  for (int t = threadIdx.x; t < nparts * G; t += blockDim.x) {
-    const int p = t / G, cc = t - p * G;
-    sm_w[t] = ws_ml[2 * (base + (int64_t)p * hq + cc)];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, sm_w[p * G + threadIdx.x]);
-    sm_M[threadIdx.x] = M;
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < nparts * G; t += blockDim.x) {
-    const int p = t / G, cc = t - p * G;
-    sm_w[t] = fast_exp2(sm_w[t] - sm_M[cc]) * ws_ml[2 * (base + (int64_t)p * hq + cc) + 1];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float den = 0.f;
-    for (int p = 0; p < nparts; ++p) den += sm_w[p * G + threadIdx.x];
-    sm_den[threadIdx.x] = den;
-  }
-  __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int cc = e / D, d = e - cc * D;
-    const float* o = ws_o + (base + cc) * D + d;
-    const int64_t step = (int64_t)hq * D;  // one partition further
-    float num = 0.f;
-    int p = 0;
-    for (; p + 4 <= nparts; p += 4) {
-      const float o0 = o[(p + 0) * step], o1 = o[(p + 1) * step];
-      const float o2 = o[(p + 2) * step], o3 = o[(p + 3) * step];
-      num += sm_w[(p + 0) * G + cc] * o0;
-      num += sm_w[(p + 1) * G + cc] * o1;
-      num += sm_w[(p + 2) * G + cc] * o2;
-      num += sm_w[(p + 3) * G + cc] * o3;
+    const int64_t row0 = base + cc;  // this head's row in partition 0; + p*hq for partition p
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += kMergeBatch) {
+      float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const int p = min(p0 + k, nparts - 1);  // past the end: re-read the last (weight 0)
+        const int64_t row = row0 + (int64_t)p * hq;
+        mp[k] = ws_ml[2 * row];
+        lp[k] = ws_ml[2 * row + 1];
+        op[k] = ws_o[row * D + d];
+      }
+      float bm = M;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, mp[k]);
+      const float f0 = fast_exp2(M - bm);  // M = -inf on the first round: 0
+      num *= f0;
+      den *= f0;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const float f = p0 + k < nparts ? fast_exp2(mp[k] - bm) * lp[k] : 0.f;
+        num += f * op[k];
+        den += f;
+      }
+      M = bm;
     }
-    for (; p < nparts; ++p) num += sm_w[p * G + cc] * o[p * step];
-    store_elem<DT>(out, ((int64_t)qb * hq + h * G + cc) * D + d, num / sm_den[cc]);
+    store_elem<DT>(out, ((int64_t)qb * hq + h * G + cc) * D + d, num / den);
   }
 }
 
@@ -239,16 +322,25 @@ template <class DT, int D, int G>
 static int launch(const AttnArgs& a) {
   typedef typename DT::T T;
   dim3 blk(256);
-  const int64_t items = (int64_t)a.num_kv_heads * a.max_parts * a.num_seqs;
-  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  DecodePlan plan;
+  plan.counts = (int32_t*)a.ws_plan;
+  plan.items = (int2*)((char*)a.ws_plan + 256);
+  plan.merge = (int32_t*)((char*)plan.items + (size_t)a.num_seqs * a.max_parts * sizeof(int2));
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
+                     a.num_seqs, a.bt_stride, a.max_parts, plan.counts, plan.items, plan.merge);
+  // grids sized for every sequence in every partition; the plan's counts cut them short
+  const int64_t units = (int64_t)a.num_kv_heads * a.max_parts * a.num_seqs;
+  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((decode_kernel<DT, D, G>), dim3((unsigned)grid), blk, 0, a.stream,
                      (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
-                     a.seq_lens, a.qsl, a.num_seqs, a.num_kv_heads, a.scale_log2, a.max_parts,
-                     a.ws_o, a.ws_ml);
-  if (a.max_parts > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<DT, D, G>), dim3(a.num_seqs * a.num_kv_heads), blk,
-                       (size_t)a.max_parts * G * sizeof(float), a.stream, (T*)a.out, a.ws_o,
-                       a.ws_ml, a.seq_lens, a.qsl, a.num_kv_heads, a.max_parts, a.bt_stride);
+                     a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, a.max_parts, a.ws_o,
+                     a.ws_ml, plan);
+  if (a.max_parts > 1) {
+    const int64_t mgrid = ((int64_t)a.num_seqs * a.num_kv_heads + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((decode_merge_kernel<DT, D, G>), dim3((unsigned)mgrid), blk, 0, a.stream,
+                       (T*)a.out, a.ws_o, a.ws_ml, a.seq_lens, a.qsl, a.num_kv_heads,
+                       a.max_parts, a.bt_stride, plan);
+  }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -277,6 +369,10 @@ static int dispatch_d(const AttnArgs& a, int D, int G) {
 
 static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
+static int64_t decode_plan_bytes(int64_t num_seqs, int64_t max_parts) {
+  return round256(256 + num_seqs * max_parts * (int64_t)sizeof(int2) + num_seqs * 4);
+}
+
 static int64_t max_partitions(int32_t max_seq_len) {
   const int64_t nb = ((int64_t)max_seq_len + kBlock - 1) / kBlock;
   const int64_t p = (nb + kPartBlocks - 1) / kPartBlocks;
@@ -294,9 +390,11 @@ extern "C" size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t 
     return 0;
   const int64_t parts = max_partitions(max_seq_len);
   const int64_t rows = (int64_t)num_seqs * parts * num_q_heads;
-  // decode (m, l) pairs, decode partition outputs, prefill work list; each 256-byte aligned
+  // decode (m, l) pairs, decode partition outputs, prefill work list, decode plan; each
+  // section 256-byte aligned
   return (size_t)(round256(rows * 2 * 4) + round256(rows * (int64_t)head_dim * 4) +
-                  round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads)));
+                  round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads)) +
+                  decode_plan_bytes(num_seqs, parts));
 }
 
 extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void* out,
@@ -322,10 +420,9 @@ extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void
   const int G = num_q_heads / cache->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
   if (cache->dtype == PKV_F32 && cache->head_dim == 256) return PKV_ERR_UNSUPPORTED;
-  // decode grid (padded to whole XCD rounds) and the merge's LDS must fit their limits
+  // the decode grid (padded to whole XCD rounds) must fit its limit
   if ((int64_t)num_seqs * cache->num_kv_heads * max_partitions(max_seq_len) + kXcds > 0x7fffffff)
     return PKV_ERR_INVALID_ARGUMENT;
-  if (max_partitions(max_seq_len) * G * (int64_t)sizeof(float) > 65536) return PKV_ERR_UNSUPPORTED;
   const size_t need = pkv_paged_attention_workspace_bytes(num_seqs, num_q_tokens, max_seq_len,
                                                           num_q_heads, cache->head_dim);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
@@ -352,6 +449,7 @@ extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void
   a.ws_o = (float*)((char*)workspace + round256(rows * 2 * 4));
   a.ws_pf = (char*)workspace + round256(rows * 2 * 4) + round256(rows * (int64_t)cache->head_dim * 4);
   a.pf_items = prefill_items_bound(num_seqs, num_q_tokens, num_q_heads);
+  a.ws_plan = (char*)a.ws_pf + round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads));
   a.stream = (hipStream_t)stream;
   // decode rows (q_len = 1), then prefill chunks: small ones per wavefront, large ones tiled
   switch (cache->dtype) {

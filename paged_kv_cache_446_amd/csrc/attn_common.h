@@ -193,6 +193,7 @@ struct AttnArgs {
   float* ws_ml;
   void* ws_pf;        // tiled-prefill work list (pf_items entries) and its queue counters
   int64_t pf_items;
+  void* ws_plan;      // decode work lists (decode_plan_kernel)
   hipStream_t stream;
 };
 
