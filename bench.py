@@ -52,6 +52,34 @@ def algorithmic_bytes(spec):
     return kv, kv + qo + table
 
 
+class ContiguousPlacer:
+    """Storage without paging, for the paging-overhead comparison: every sequence
+    gets one run of consecutive blocks sized for its final length, in sequence
+    order.  Offers the allocator calls a workload flow issues; no sharing."""
+
+    def __init__(self, final_lens):
+        self.nb = -(-np.asarray(final_lens, dtype=np.int64) // 16)
+        self.first = np.concatenate([[0], np.cumsum(self.nb)[:-1]]).astype(np.int32)
+        self._next = 0
+
+    def new_table(self, cap):
+        s = self._next
+        self._next += 1
+        t = np.full(cap, -1, dtype=np.int32)
+        t[: self.nb[s]] = self.first[s] + np.arange(self.nb[s])
+        return t
+
+    def append_slots(self, table, nblk, seq_len, n_new):
+        pos = np.arange(seq_len, seq_len + n_new, dtype=np.int64)
+        slots = table[pos // 16].astype(np.int64) * 16 + pos % 16
+        return int(-(-(seq_len + n_new) // 16)), seq_len + n_new, slots, np.zeros((0, 2), np.int32)
+
+    def fork(self, table, nblk):
+        raise ValueError("contiguous placement has no shared blocks")
+
+    make_writable = fork
+
+
 def measured_traffic():
     """HBM bytes per paged_attention launch from the committed counter summary,
     or None if the kernel sources changed since the counters were taken."""
@@ -135,11 +163,18 @@ def main():
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
+                    help="random: blocks from a seeded permutation of the pool (paged); "
+                         "contiguous: each sequence in one run of consecutive blocks")
+    ap.add_argument("--kernel", default="paged", choices=["paged", "contiguous"],
+                    help="contiguous: the table-free baseline (needs --placement contiguous)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a kernel of known size for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
+    if args.kernel == "contiguous" and args.placement != "contiguous":
+        ap.error("--kernel contiguous needs --placement contiguous")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this path runs on a single MI355X with no sharding "
@@ -160,8 +195,14 @@ def main():
         f"pool blocks={spec.num_blocks}")
 
     # ---- host allocator (a1): timed on its own ----------------------------
-    alloc = BlockAllocator(spec.num_blocks, free_order=spec.free_order)
-    flow = workloads.run_flow(spec, alloc)
+    if args.placement == "contiguous":
+        if spec.shared_prefix:
+            raise SystemExit("contiguous placement: this workload shares blocks")
+        placer = ContiguousPlacer(spec.seq_lens)
+        flow = workloads.run_flow(spec, placer)
+    else:
+        alloc = BlockAllocator(spec.num_blocks, free_order=spec.free_order)
+        flow = workloads.run_flow(spec, alloc)
     # per-step host cost: one batched append of the step's tokens on a copy of the state
     probe = BlockAllocator(spec.num_blocks, free_order=spec.free_order)
     pflow_tables = np.stack([t.copy() for t in workloads.run_flow(spec, probe).tables])
@@ -203,9 +244,18 @@ def main():
     ws = torch.empty(ops.workspace_bytes(S, spec.num_q_tokens, max_n, spec.num_q_heads, spec.head_dim),
                      dtype=torch.uint8, device=dev)
 
-    def attention():
-        ops.paged_attention(cache, out, q, tables, seq_lens, qsl, num_q_heads=spec.num_q_heads,
-                            max_q_len=max_q, max_seq_len=max_n, scale=spec.scale, workspace=ws)
+    if args.kernel == "contiguous":
+        first_block = torch.from_numpy(placer.first).to(dev)
+
+        def attention():
+            ops.contiguous_attention(cache, out, q, first_block, seq_lens, qsl,
+                                     num_q_heads=spec.num_q_heads, max_seq_len=max_n,
+                                     scale=spec.scale, workspace=ws)
+    else:
+        def attention():
+            ops.paged_attention(cache, out, q, tables, seq_lens, qsl, num_q_heads=spec.num_q_heads,
+                                max_q_len=max_q, max_seq_len=max_n, scale=spec.scale,
+                                workspace=ws)
 
     def step(ev_a=None, ev_b=None):
         if step_pairs is not None:
@@ -273,19 +323,23 @@ def main():
             "block_size": 16,
             "pool_blocks": spec.num_blocks,
             "step": "copy_blocks (CoW pairs, if any) + kv_cache_write + paged_attention",
+            "placement": args.placement,
+            "kernel": args.kernel,
         },
         "tokens_per_s": round(spec.num_q_tokens / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(int(spec.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "host_alloc_us": round(host_alloc_us, 1),
         "roofline": {
-            "kernel": "paged_attention (decode partition kernel + partition merge)",
+            "kernel": ("contiguous_attention" if args.kernel == "contiguous" else "paged_attention") +
+                      " (plan + decode partition kernel + partition merge)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic() if args.config == "c3" else None,
+            "traffic": measured_traffic() if (args.config, args.placement, args.kernel) ==
+            ("c3", "random", "paged") else None,
             "algorithmic_bytes_per_launch": attn_bytes,
             "avg_launch_us": round(attn_avg * 1e3, 2),
         },

@@ -149,6 +149,25 @@ int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void* out, cons
                         int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads, float scale,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * contiguous_attention: the baseline the pages compare paging against -- every
+ * sequence's K/V stored as one contiguous run of blocks, reached without a block
+ * table ([blog] "PagedAttention": paged reads give the same result as contiguous
+ * storage at a per-kernel cost).  Decode rows only.
+ *   first_block    device int32 [num_seqs]: block j of sequence s is first_block[s] + j
+ *   other arguments as for pkv_paged_attention (max_q_len is 1)
+ * Same kernels and arithmetic as pkv_paged_attention: on a pool whose sequences
+ * occupy consecutive blocks the two give identical bits.  Rows of sequences with
+ * q_len != 1 are not written.  Preconditions (not checked on the device):
+ * first_block[s] + ceil(seq_len/16) <= num_blocks.  Workspace as for
+ * pkv_paged_attention_workspace_bytes(num_seqs, num_q_tokens, max_seq_len, ...).
+ */
+int pkv_contiguous_attention(const pkv_cache_t* cache, int32_t layer, void* out, const void* q,
+                             const int32_t* first_block, const int32_t* seq_lens,
+                             const int32_t* query_start_loc, int32_t num_seqs,
+                             int32_t num_q_tokens, int32_t max_seq_len, int32_t num_q_heads,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_paged_attention needs for these bounds (0 on bad input). */
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens,
                                            int32_t max_seq_len, int32_t num_q_heads,

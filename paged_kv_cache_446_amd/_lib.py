@@ -25,7 +25,8 @@ DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 # every symbol include/pkv.h declares
 EXPORTS = (
     "pkv_status_string", "pkv_pool_bytes", "pkv_kv_cache_write", "pkv_copy_blocks",
-    "pkv_paged_attention", "pkv_paged_attention_workspace_bytes", "pkv_ba_create",
+    "pkv_paged_attention", "pkv_contiguous_attention", "pkv_paged_attention_workspace_bytes",
+    "pkv_ba_create",
     "pkv_ba_destroy", "pkv_ba_alloc", "pkv_ba_incref", "pkv_ba_decref", "pkv_ba_refcount",
     "pkv_ba_num_free", "pkv_ba_num_blocks", "pkv_blocks_for_tokens", "pkv_seq_append_slots",
     "pkv_batch_append_slots", "pkv_seq_make_writable", "pkv_seq_fork", "pkv_seq_free",
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
         "pkv_copy_blocks": (ctypes.c_int, [pcache, P, i32, P]),
         "pkv_paged_attention": (ctypes.c_int, [pcache, i32, P, P, P, i32, P, P, i32, i32, i32, i32,
                                                i32, f32, P, sz, P]),
+        "pkv_contiguous_attention": (ctypes.c_int, [pcache, i32, P, P, P, P, P, i32, i32, i32, i32,
+                                                    f32, P, sz, P]),
         "pkv_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "pkv_ba_create": (ctypes.c_int, [i32, i32, pi32, ctypes.POINTER(P)]),
         "pkv_ba_destroy": (None, [P]),

@@ -145,7 +145,8 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
                    const int32_t* __restrict__ bt, int bt_stride,
                    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
                    int num_kv_heads, float scale_log2, int max_parts,
-                   float* __restrict__ ws_o, float* __restrict__ ws_ml, DecodePlan plan) {
+                   float* __restrict__ ws_o, float* __restrict__ ws_ml, DecodePlan plan,
+                   int contiguous) {
   typedef Geo<DT, D> Gm;
   const int j = xcd_unit(blockIdx.x, plan.counts[0] * num_kv_heads);
   if (j < 0) return;
@@ -157,11 +158,13 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
   const int b0 = part * kPartBlocks;
   const int32_t* btr = bt + (int64_t)s * bt_stride;
   // block-table entries of this wavefront's blocks b0 + w + 4i, one per lane,
-  // loaded alongside the sequence metadata (bounded by the table width only)
+  // loaded alongside the sequence metadata (bounded by the table width only).
+  // Contiguous storage (the baseline without paging): bt[s] is the sequence's
+  // first block and block i is bt[s] + i.
   int btv = 0;
   {
     const int bi = b0 + w + kWaves * lane;
-    if (lane < kPerWave && bi < bt_stride) btv = btr[bi];
+    if (lane < kPerWave && bi < bt_stride) btv = contiguous ? bt[s] + bi : btr[bi];
   }
   const int qb = qsl[s];
   if (qsl[s + 1] - qb != 1) return;
@@ -334,7 +337,7 @@ static int launch(const AttnArgs& a) {
   hipLaunchKernelGGL((decode_kernel<DT, D, G>), dim3((unsigned)grid), blk, 0, a.stream,
                      (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
                      a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, a.max_parts, a.ws_o,
-                     a.ws_ml, plan);
+                     a.ws_ml, plan, a.contiguous);
   if (a.max_parts > 1) {
     const int64_t mgrid = ((int64_t)a.num_seqs * a.num_kv_heads + kXcds - 1) / kXcds * kXcds;
     hipLaunchKernelGGL((decode_merge_kernel<DT, D, G>), dim3((unsigned)mgrid), blk, 0, a.stream,
@@ -397,12 +400,12 @@ extern "C" size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t 
                   decode_plan_bytes(num_seqs, parts));
 }
 
-extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void* out,
-                                   const void* q, const int32_t* block_tables, int32_t bt_stride,
-                                   const int32_t* seq_lens, const int32_t* query_start_loc,
-                                   int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
-                                   int32_t max_seq_len, int32_t num_q_heads, float scale,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+static int attention_impl(const pkv_cache_t* cache, int32_t layer, void* out, const void* q,
+                          const int32_t* block_tables, int32_t bt_stride, int contiguous,
+                          const int32_t* seq_lens, const int32_t* query_start_loc,
+                          int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
+                          int32_t max_seq_len, int32_t num_q_heads, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
   if (layer < 0 || layer >= cache->num_layers) return PKV_ERR_INVALID_ARGUMENT;
@@ -437,6 +440,7 @@ extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void
   a.vp = (const char*)cache->v_pool + layer_elems * eb;
   a.bt = block_tables;
   a.bt_stride = bt_stride;
+  a.contiguous = contiguous;
   a.seq_lens = seq_lens;
   a.qsl = query_start_loc;
   a.num_seqs = num_seqs;
@@ -462,4 +466,28 @@ extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void
   rc = launch_prefill_small(a, cache->dtype, cache->head_dim, G);
   if (rc != PKV_OK || (int64_t)max_q_len * G <= kSmallChunkCols) return rc;
   return launch_prefill_tiled(a, cache->dtype, cache->head_dim, G);
+}
+
+extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void* out,
+                                   const void* q, const int32_t* block_tables, int32_t bt_stride,
+                                   const int32_t* seq_lens, const int32_t* query_start_loc,
+                                   int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
+                                   int32_t max_seq_len, int32_t num_q_heads, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(cache, layer, out, q, block_tables, bt_stride, 0, seq_lens,
+                        query_start_loc, num_seqs, num_q_tokens, max_q_len, max_seq_len,
+                        num_q_heads, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_contiguous_attention(const pkv_cache_t* cache, int32_t layer, void* out,
+                                        const void* q, const int32_t* first_block,
+                                        const int32_t* seq_lens, const int32_t* query_start_loc,
+                                        int32_t num_seqs, int32_t num_q_tokens,
+                                        int32_t max_seq_len, int32_t num_q_heads, float scale,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  // decode rows only: the same kernels, the blocks of a sequence addressed as one run
+  const int32_t run = (int32_t)(((int64_t)max_seq_len + kBlock - 1) / kBlock);
+  return attention_impl(cache, layer, out, q, first_block, run > 0 ? run : 1, 1, seq_lens,
+                        query_start_loc, num_seqs, num_q_tokens, 1, max_seq_len, num_q_heads,
+                        scale, workspace, workspace_bytes, stream);
 }

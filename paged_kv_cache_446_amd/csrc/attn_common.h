@@ -183,8 +183,9 @@ struct AttnArgs {
   void* out;
   const void* kp;
   const void* vp;
-  const int32_t* bt;
+  const int32_t* bt;  // block tables, or first blocks of contiguous runs (contiguous != 0)
   int bt_stride;
+  int contiguous;
   const int32_t* seq_lens;
   const int32_t* qsl;
   int num_seqs, num_kv_heads, max_q_len, max_parts;

@@ -85,3 +85,20 @@ def paged_attention(cache: PagedCache, out, q, block_tables, seq_lens, query_sta
                                        num_q_heads, float(scale), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)),
                "pkv_paged_attention")
+
+
+def contiguous_attention(cache: PagedCache, out, q, first_block, seq_lens, query_start_loc, *,
+                         num_q_heads: int, max_seq_len: int, scale: float, workspace, layer: int = 0,
+                         stream=None):
+    """Decode attention over sequences stored as contiguous block runs (no block table)."""
+    lib = _lib.load()
+    for t in (first_block, seq_lens, query_start_loc):
+        assert t.dtype == torch.int32 and t.is_contiguous() and t.is_cuda
+    assert q.is_contiguous() and out.is_contiguous()
+    S = seq_lens.numel()
+    Tq = q.numel() // (num_q_heads * cache.head_dim)
+    _lib.check(lib.pkv_contiguous_attention(ctypes.byref(cache.desc), layer, _ptr(out), _ptr(q),
+                                            _ptr(first_block), _ptr(seq_lens), _ptr(query_start_loc),
+                                            S, Tq, max_seq_len, num_q_heads, float(scale),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream)), "pkv_contiguous_attention")
