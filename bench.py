@@ -34,6 +34,7 @@ WORKLOAD_NAMES = {
     "c3": "Llama-3-8B-shaped GQA decode: 256 seqs, context log-uniform [64,8192], 32q/8kv heads, head_dim 128, bf16",
     "c4": "shared-prefix parallel sampling: 64 seqs share a 10000-token prefix + U[0,256] private tails, CoW, 32q/8kv, bf16",
     "c5": "mixed chunked-prefill + decode: 16 chunks q U[16,512] over context U[0,32768] + 128 decodes U[64,8192], 32q/8kv, bf16",
+    "prefix-cache": "repeated 10000-token prompt + 256 new tokens (second request), 32q/8kv heads, head_dim 128, bf16",
 }
 
 
@@ -155,6 +156,94 @@ def cpu_baseline(spec, out_bits, target_s):
     return base, parity
 
 
+def bench_prefix_cache(args):
+    """A repeated ~10,000-token prompt (the pages' prefix-caching example) with 256
+    new tokens, one attention layer: the second request's cache write + prefill
+    attention with its prefix served from the cache, and without the cache."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_446_amd import ops
+    from paged_kv_cache_446_amd.allocator import BlockAllocator
+    from tests.gpu_pipeline import dev_bits
+
+    dev = "cuda:0"
+    P, tail, hq, hkv, D = 10000, 256, 32, 8, 128
+    n = P + tail
+    spec = workloads.make_spec("prefix-cache", (446, 60), "bf16", hq, hkv, D, [n - tail, 0], [tail, n],
+                               shared_prefix=P)
+    rng = np.random.default_rng([446, 61])
+    prompt = rng.integers(0, 32000, size=P).astype(np.int32)
+    tokens = np.concatenate([prompt, rng.integers(0, 32000, size=tail).astype(np.int32)])
+    nblocks = 4 * (-(-n // 16))
+    alloc = BlockAllocator(nblocks, free_order=np.random.default_rng([446, 62]).permutation(nblocks)
+                           .astype(np.int32))
+    kp = torch.zeros(nblocks * hkv * 16 * D, dtype=torch.int16, device=dev)
+    vp = torch.zeros_like(kp)
+    cache = ops.PagedCache(kp, vp, hkv, D, dtype="bf16")
+    cap = -(-n // 16) + 1
+    # the first request: its prompt written and sealed, then finished
+    t1 = alloc.new_table(cap)
+    nb1, _, s1, _ = alloc.append_slots(t1, 0, 0, P)
+    k, v = spec.kv_bits(1, 0, P)
+    ops.kv_cache_write(cache, dev_bits(k, "bf16"), dev_bits(v, "bf16"), torch.from_numpy(s1).to(dev))
+    alloc.cache_seal(prompt, t1, nb1)
+    alloc.free_seq(t1, nb1)
+    # the second request, served from the cache (host time measured)
+    t0 = time.perf_counter()
+    t2 = alloc.new_table(cap)
+    hit = alloc.cache_lookup(tokens, t2)
+    nb2, _, s2, _ = alloc.append_slots(t2, hit, hit * 16, n - hit * 16)
+    lookup_us = (time.perf_counter() - t0) * 1e6
+    # and without the cache: the whole prompt in fresh blocks
+    t3 = alloc.new_table(cap)
+    nb3, _, s3, _ = alloc.append_slots(t3, 0, 0, n)
+    kc, vc = spec.kv_bits(1, hit * 16, n)
+    kf, vf = spec.kv_bits(1, 0, n)
+    q_all = spec.q_bits(1)  # [n][Hq][D]: the uncached prefill queries every prompt token
+    modes = {
+        "cached": dict(k=dev_bits(kc, "bf16"), v=dev_bits(vc, "bf16"), slots=torch.from_numpy(s2).to(dev),
+                       table=torch.from_numpy(t2[None, :nb2].copy()).to(dev), q=dev_bits(q_all[n - (n - hit * 16):], "bf16")),
+        "uncached": dict(k=dev_bits(kf, "bf16"), v=dev_bits(vf, "bf16"), slots=torch.from_numpy(s3).to(dev),
+                         table=torch.from_numpy(t3[None, :nb3].copy()).to(dev), q=dev_bits(q_all, "bf16")),
+    }
+    seq_lens = torch.tensor([n], dtype=torch.int32, device=dev)
+    res = {}
+    for name, m in modes.items():
+        qn = m["q"].shape[0]
+        qsl = torch.tensor([0, qn], dtype=torch.int32, device=dev)
+        out = torch.zeros_like(m["q"])
+        ws = torch.empty(ops.workspace_bytes(1, qn, n, hq, D), dtype=torch.uint8, device=dev)
+
+        def step():
+            ops.kv_cache_write(cache, m["k"], m["v"], m["slots"])
+            ops.paged_attention(cache, out, m["q"], m["table"], seq_lens, qsl, num_q_heads=hq,
+                                max_q_len=qn, max_seq_len=n, scale=spec.scale, workspace=ws)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = dict(ms=a.elapsed_time(b) / args.steps, query_tokens=qn)
+        log(f"{name}: {qn} query tokens over {n} keys: {res[name]['ms']:.3f} ms")
+    print(json.dumps({
+        "metric": "second request of a repeated 10,000-token prompt: cache write + prefill attention "
+                  "(one layer), prefix cache on vs off",
+        "value": round(res["cached"]["ms"], 4), "unit": "ms", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+        "without_cache_ms": round(res["uncached"]["ms"], 4),
+        "speedup": round(res["uncached"]["ms"] / res["cached"]["ms"], 2),
+        "cached_blocks": hit, "host_lookup_and_append_us": round(lookup_us, 1),
+        "config": {"workload": WORKLOAD_NAMES["prefix-cache"], "num_q_heads": hq, "num_kv_heads": hkv,
+                   "head_dim": D, "block_size": 16},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +278,8 @@ def main():
     from tests.gpu_pipeline import dev_bits, host_bits
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.config == "prefix-cache":
+        return bench_prefix_cache(args)
     dev = "cuda:0"
     spec = workloads.named_spec(args.config)
     log(f"workload {args.config}: S={spec.num_seqs} context tokens={int(spec.seq_lens.sum())} "

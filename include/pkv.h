@@ -251,6 +251,46 @@ int pkv_seq_fork(pkv_ba_t* ba, const int32_t* src_table, int32_t nblk, int32_t* 
  * reaching zero return to the free pool.  All or nothing. */
 int pkv_seq_free(pkv_ba_t* ba, const int32_t* table, int32_t nblk);
 
+/* ---- prefix cache (host) --------------------------------------------------- */
+/*
+ * Hash-based automatic prefix caching: a request whose prompt begins with the
+ * same tokens as an earlier one reuses the earlier request's full KV blocks
+ * instead of recomputing them ([blog] advanced features and V1: prefix caching
+ * by hash, on by default; [devpress] sharing section: prompt caching).
+ *
+ * A full block is sealed with the 16 token ids it holds and its parent (the
+ * block before it in the sequence, -1 for the first).  A sealed block stays in
+ * the cache while it is in use and after its count drops to zero; the free
+ * pool hands out the block released longest ago first, and a cached block
+ * taken that way leaves the cache (least-recently-released eviction).  The
+ * contents of a sealed block must not change.
+ */
+
+/* Chained 64-bit hash of one block's 16 token ids after a parent hash (0 for
+ * the first block).  Lookups locate candidates with it and then compare parent
+ * and token ids exactly, so a hash collision cannot produce a wrong hit. */
+uint64_t pkv_prefix_hash(uint64_t parent_hash, const int32_t* tokens16);
+
+/* Start a new sequence from the cache: walk the full blocks of its prompt
+ * tokens[0..num_tokens) in order and take each cached block that continues the
+ * chain (count + 1; a free cached block leaves the free pool), stopping at the
+ * first miss or at cap blocks.  table[0..*nblk) receives the blocks; the
+ * sequence then holds *nblk * 16 cached tokens and appends the rest with
+ * pkv_seq_append_slots.  Never allocates, so it cannot run out of blocks. */
+int pkv_seq_cache_lookup(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens, int32_t* table,
+                         int32_t cap, int32_t* nblk);
+
+/* Register the full blocks of a sequence (table[0..nblk) holding
+ * tokens[0..num_tokens)) in the cache once their K/V are written.  Blocks
+ * already cached must hold the same tokens after the same parent
+ * (PKV_ERR_INVALID_ARGUMENT otherwise, and nothing changes); a block whose
+ * content is cached under another block stays out of the cache. */
+int pkv_seq_cache_seal(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens,
+                       const int32_t* table, int32_t nblk);
+
+/* Blocks currently in the cache (in use or free). */
+int32_t pkv_ba_num_cached(const pkv_ba_t* ba);
+
 #ifdef __cplusplus
 }
 #endif

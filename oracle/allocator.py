@@ -81,7 +81,7 @@ class BlockAllocatorModel:
     def alloc(self) -> int:
         if not self.free:
             raise OutOfBlocks()
-        b = self.free.popleft()
+        b = self._take_front()
         self.ref[b] = 1
         return b
 
@@ -172,6 +172,67 @@ class BlockAllocatorModel:
                     self.free.pop()
                 self.ref[b] += 1
             raise
+
+    # ---- prefix cache -------------------------------------------------------
+    # A full block is cached under the exact key (parent block, its 16 token ids):
+    # a later prompt starting with the same tokens finds the same chain of blocks
+    # (blog.mckayzhao.com/?p=56, advanced features and V1 sections: hash-based
+    # automatic prefix caching; devpress page, sharing section).  Cached blocks
+    # stay findable after their count drops to zero; the free queue hands out the
+    # block released longest ago first, which leaves the cache.
+
+    def _cache(self):
+        if not hasattr(self, "key_of"):
+            self.key_of = {}   # block -> key
+            self.block_of = {}  # key -> block
+        return self.key_of, self.block_of
+
+    def _take_front(self) -> int:
+        b = self.free.popleft()
+        key_of, block_of = self._cache()
+        if b in key_of:
+            del block_of[key_of.pop(b)]
+        return b
+
+    def cache_lookup(self, tokens, table) -> int:
+        key_of, block_of = self._cache()
+        tokens = [int(t) for t in tokens]
+        n = min(len(tokens) // BLOCK_SIZE, len(table))
+        j = 0
+        while j < n:
+            key = (int(table[j - 1]) if j else -1, tuple(tokens[j * BLOCK_SIZE:(j + 1) * BLOCK_SIZE]))
+            b = block_of.get(key)
+            if b is None:
+                break
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            table[j] = b
+            j += 1
+        return j
+
+    def cache_seal(self, tokens, table, nblk: int):
+        key_of, block_of = self._cache()
+        tokens = [int(t) for t in tokens]
+        n = min(len(tokens) // BLOCK_SIZE, nblk)
+        keys = [(int(table[j - 1]) if j else -1, tuple(tokens[j * BLOCK_SIZE:(j + 1) * BLOCK_SIZE]))
+                for j in range(n)]
+        for j in range(n):
+            b = int(table[j])
+            self._check_id(b)
+            if self.ref[b] <= 0:
+                raise RefcountError("table holds a free block")
+            if b in key_of and key_of[b] != keys[j]:
+                raise InvalidArgument("a cached block must keep its contents")
+        for j in range(n):
+            b = int(table[j])
+            if b in key_of or keys[j] in block_of:
+                continue
+            key_of[b] = keys[j]
+            block_of[keys[j]] = b
+
+    def num_cached(self) -> int:
+        return len(self._cache()[0])
 
     # ---- statistics ---------------------------------------------------------
     @staticmethod

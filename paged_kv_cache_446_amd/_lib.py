@@ -30,6 +30,7 @@ EXPORTS = (
     "pkv_ba_destroy", "pkv_ba_alloc", "pkv_ba_incref", "pkv_ba_decref", "pkv_ba_refcount",
     "pkv_ba_num_free", "pkv_ba_num_blocks", "pkv_blocks_for_tokens", "pkv_seq_append_slots",
     "pkv_batch_append_slots", "pkv_seq_make_writable", "pkv_seq_fork", "pkv_seq_free",
+    "pkv_prefix_hash", "pkv_seq_cache_lookup", "pkv_seq_cache_seal", "pkv_ba_num_cached",
 )
 
 
@@ -91,6 +92,10 @@ def load() -> ctypes.CDLL:
         "pkv_seq_make_writable": (ctypes.c_int, [P, pi32, i32, i32, pi32, pi32]),
         "pkv_seq_fork": (ctypes.c_int, [P, pi32, i32, pi32]),
         "pkv_seq_free": (ctypes.c_int, [P, pi32, i32]),
+        "pkv_prefix_hash": (ctypes.c_uint64, [ctypes.c_uint64, pi32]),
+        "pkv_seq_cache_lookup": (ctypes.c_int, [P, pi32, i32, pi32, i32, pi32]),
+        "pkv_seq_cache_seal": (ctypes.c_int, [P, pi32, i32, pi32, i32]),
+        "pkv_ba_num_cached": (i32, [P]),
     }
     for name in EXPORTS:
         fn = getattr(lib, name)

@@ -112,3 +112,29 @@ class BlockAllocator:
 
     def free_seq(self, table: np.ndarray, nblk: int):
         _lib.check(self._lib.pkv_seq_free(self._h, _p32(table), int(nblk)), "pkv_seq_free")
+
+    # ---- prefix cache ------------------------------------------------------------
+    def cache_lookup(self, tokens: np.ndarray, table: np.ndarray) -> int:
+        """Take the cached full blocks that start this prompt; returns how many."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        nb = ctypes.c_int32(0)
+        _lib.check(self._lib.pkv_seq_cache_lookup(self._h, _p32(tokens) if len(tokens) else None,
+                                                  len(tokens), _p32(table), len(table),
+                                                  ctypes.byref(nb)), "pkv_seq_cache_lookup")
+        return nb.value
+
+    def cache_seal(self, tokens: np.ndarray, table: np.ndarray, nblk: int):
+        """Register the sequence's full blocks (their K/V written) in the cache."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        _lib.check(self._lib.pkv_seq_cache_seal(self._h, _p32(tokens) if len(tokens) else None,
+                                                len(tokens), _p32(table), int(nblk)),
+                   "pkv_seq_cache_seal")
+
+    def num_cached(self) -> int:
+        return int(self._lib.pkv_ba_num_cached(self._h))
+
+
+def prefix_hash(parent: int, tokens16) -> int:
+    t = np.ascontiguousarray(tokens16, dtype=np.int32)
+    assert t.shape == (16,)
+    return int(_lib.load().pkv_prefix_hash(ctypes.c_uint64(parent), _p32(t)))

@@ -9,9 +9,21 @@
  * "PagedAttention").  Shared blocks carry reference counts and are copied
  * before a sequence modifies them (same blog page, copy-on-write section).
  *
- * Free pool: a FIFO ring of block ids.  Allocation pops the front; a block
- * whose count reaches zero is pushed at the back.
+ * Free pool: a FIFO queue of block ids (a doubly linked list over block ids, so
+ * that a cached block can leave it from the middle).  Allocation pops the
+ * front; a block whose count reaches zero is pushed at the back, so the front
+ * is the block released longest ago.
+ *
+ * Prefix cache (hash-based automatic prefix caching: blog page, advanced
+ * features and V1 sections; devpress page, sharing section, prompt caching):
+ * a full block can be sealed with the 16 token ids it holds and its parent
+ * (the block before it in the sequence).  Sealed blocks stay findable after
+ * their count drops to zero, until allocation takes them from the front of the
+ * free queue (least recently released first).  A lookup walks a new prompt's
+ * full blocks, finding each by a chained 64-bit hash and verifying parent and
+ * token ids exactly.
  */
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -20,25 +32,112 @@
 struct pkv_ba {
   int32_t num_blocks;
   int32_t* ref;  /* [num_blocks] reference counts, 0 = free */
-  int32_t* ring; /* [num_blocks] free queue storage */
-  int32_t head;  /* index of the front element */
-  int32_t count; /* number of free blocks */
+  int32_t* next; /* [num_blocks] free queue links (-1 = none) */
+  int32_t* prev;
+  int32_t head, tail; /* front and back of the free queue (-1 if empty) */
+  int32_t count;      /* number of free blocks */
+  /* prefix cache */
+  uint8_t* sealed;   /* [num_blocks] 1 if the block is in the cache */
+  uint64_t* hash;    /* [num_blocks] chained hash of the block's tokens */
+  int32_t* parent;   /* [num_blocks] previous block of the sequence, -1 for the first */
+  int32_t* tokens;   /* [num_blocks][16] token ids */
+  int32_t* slot;     /* [hcap] open-addressing table of sealed block ids; -1 empty, -2 deleted */
+  int64_t hcap;      /* power of two >= 2 * num_blocks */
+  int32_t num_sealed;
+  int64_t num_deleted; /* deleted slots (the table is rebuilt when they pile up) */
 };
 
-static int32_t ring_pop_front(pkv_ba_t* ba) {
-  int32_t b = ba->ring[ba->head];
-  ba->head = (ba->head + 1) % ba->num_blocks;
+static void q_remove(pkv_ba_t* ba, int32_t b) {
+  const int32_t p = ba->prev[b], n = ba->next[b];
+  if (p >= 0) ba->next[p] = n; else ba->head = n;
+  if (n >= 0) ba->prev[n] = p; else ba->tail = p;
+  ba->next[b] = ba->prev[b] = -1;
   ba->count--;
+}
+
+static void unseal(pkv_ba_t* ba, int32_t b);
+
+static int32_t q_pop_front(pkv_ba_t* ba) {
+  const int32_t b = ba->head;
+  q_remove(ba, b);
+  if (ba->sealed[b]) unseal(ba, b); /* the least recently released cached block is evicted */
   return b;
 }
 
-static void ring_push_back(pkv_ba_t* ba, int32_t b) {
-  ba->ring[(ba->head + ba->count) % ba->num_blocks] = b;
+static void q_push_back(pkv_ba_t* ba, int32_t b) {
+  ba->prev[b] = ba->tail;
+  ba->next[b] = -1;
+  if (ba->tail >= 0) ba->next[ba->tail] = b; else ba->head = b;
+  ba->tail = b;
   ba->count++;
 }
 
 /* undo the newest push_back (the block must be at the back) */
-static void ring_pop_back(pkv_ba_t* ba) { ba->count--; }
+static void q_pop_back(pkv_ba_t* ba) { q_remove(ba, ba->tail); }
+
+/* ---- prefix-cache hash table ------------------------------------------------ */
+
+/* the splitmix64 output function (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", 2014) as a 64-bit mixer */
+static uint64_t mix64(uint64_t z) {
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+uint64_t pkv_prefix_hash(uint64_t parent_hash, const int32_t* tokens) {
+  uint64_t h = mix64(parent_hash ^ 0x243F6A8885A308D3ull);
+  for (int i = 0; i < PKV_BLOCK_SIZE; ++i) h = mix64(h ^ (uint32_t)tokens[i]);
+  return h;
+}
+
+/* sealed block equal to (h, parent, tokens), or -1 */
+static int32_t find_sealed(const pkv_ba_t* ba, uint64_t h, int32_t parent, const int32_t* tokens) {
+  for (int64_t i = (int64_t)(h & (uint64_t)(ba->hcap - 1)), k = 0; k < ba->hcap;
+       i = (i + 1) & (ba->hcap - 1), ++k) {
+    const int32_t b = ba->slot[i];
+    if (b == -1) return -1;
+    if (b >= 0 && ba->hash[b] == h && ba->parent[b] == parent &&
+        memcmp(ba->tokens + (int64_t)b * PKV_BLOCK_SIZE, tokens, PKV_BLOCK_SIZE * sizeof(int32_t)) == 0)
+      return b;
+  }
+  return -1;
+}
+
+static void slot_insert(pkv_ba_t* ba, int32_t b) {
+  int64_t i = (int64_t)(ba->hash[b] & (uint64_t)(ba->hcap - 1));
+  while (ba->slot[i] >= 0) i = (i + 1) & (ba->hcap - 1);
+  if (ba->slot[i] == -2) ba->num_deleted--;
+  ba->slot[i] = b;
+}
+
+/* rebuild the table without deleted slots (keeps probe sequences short) */
+static void rehash(pkv_ba_t* ba) {
+  for (int64_t i = 0; i < ba->hcap; ++i) ba->slot[i] = -1;
+  ba->num_deleted = 0;
+  for (int32_t b = 0; b < ba->num_blocks; ++b)
+    if (ba->sealed[b]) slot_insert(ba, b);
+}
+
+static void seal(pkv_ba_t* ba, int32_t b, uint64_t h, int32_t parent, const int32_t* tokens) {
+  if (4 * (ba->num_sealed + 1 + ba->num_deleted) > 3 * ba->hcap) rehash(ba);
+  ba->hash[b] = h;
+  slot_insert(ba, b);
+  ba->sealed[b] = 1;
+  ba->parent[b] = parent;
+  memcpy(ba->tokens + (int64_t)b * PKV_BLOCK_SIZE, tokens, PKV_BLOCK_SIZE * sizeof(int32_t));
+  ba->num_sealed++;
+}
+
+static void unseal(pkv_ba_t* ba, int32_t b) {
+  int64_t i = (int64_t)(ba->hash[b] & (uint64_t)(ba->hcap - 1));
+  while (ba->slot[i] != b) i = (i + 1) & (ba->hcap - 1);
+  ba->slot[i] = -2;
+  ba->num_deleted++;
+  ba->sealed[b] = 0;
+  ba->num_sealed--;
+}
 
 int64_t pkv_blocks_for_tokens(int64_t n, int32_t block_size) {
   if (n < 0 || block_size <= 0) return -1;
@@ -52,13 +151,25 @@ int pkv_ba_create(int32_t num_blocks, int32_t block_size, const int32_t* free_or
   if (num_blocks <= 0 || block_size != PKV_BLOCK_SIZE) return PKV_ERR_INVALID_ARGUMENT;
   pkv_ba_t* ba = (pkv_ba_t*)calloc(1, sizeof(pkv_ba_t));
   if (!ba) return PKV_ERR_INVALID_ARGUMENT;
-  ba->ref = (int32_t*)calloc((size_t)num_blocks, sizeof(int32_t));
-  ba->ring = (int32_t*)malloc((size_t)num_blocks * sizeof(int32_t));
-  if (!ba->ref || !ba->ring) {
+  const size_t nb = (size_t)num_blocks;
+  ba->hcap = 2;
+  while (ba->hcap < 2 * (int64_t)num_blocks) ba->hcap *= 2;
+  ba->ref = (int32_t*)calloc(nb, sizeof(int32_t));
+  ba->next = (int32_t*)malloc(nb * sizeof(int32_t));
+  ba->prev = (int32_t*)malloc(nb * sizeof(int32_t));
+  ba->sealed = (uint8_t*)calloc(nb, 1);
+  ba->hash = (uint64_t*)calloc(nb, sizeof(uint64_t));
+  ba->parent = (int32_t*)calloc(nb, sizeof(int32_t));
+  ba->tokens = (int32_t*)calloc(nb * PKV_BLOCK_SIZE, sizeof(int32_t));
+  ba->slot = (int32_t*)malloc((size_t)ba->hcap * sizeof(int32_t));
+  if (!ba->ref || !ba->next || !ba->prev || !ba->sealed || !ba->hash || !ba->parent ||
+      !ba->tokens || !ba->slot) {
     pkv_ba_destroy(ba);
     return PKV_ERR_INVALID_ARGUMENT;
   }
+  for (int64_t i = 0; i < ba->hcap; ++i) ba->slot[i] = -1;
   ba->num_blocks = num_blocks;
+  ba->head = ba->tail = -1;
   for (int32_t i = 0; i < num_blocks; ++i) {
     int32_t b = free_order ? free_order[i] : i;
     /* free_order must be a permutation: use ref[] as the seen-set */
@@ -67,11 +178,9 @@ int pkv_ba_create(int32_t num_blocks, int32_t block_size, const int32_t* free_or
       return PKV_ERR_INVALID_ARGUMENT;
     }
     ba->ref[b] = 1;
-    ba->ring[i] = b;
+    q_push_back(ba, b);
   }
-  memset(ba->ref, 0, (size_t)num_blocks * sizeof(int32_t));
-  ba->head = 0;
-  ba->count = num_blocks;
+  memset(ba->ref, 0, nb * sizeof(int32_t));
   *out = ba;
   return PKV_OK;
 }
@@ -79,7 +188,13 @@ int pkv_ba_create(int32_t num_blocks, int32_t block_size, const int32_t* free_or
 void pkv_ba_destroy(pkv_ba_t* ba) {
   if (!ba) return;
   free(ba->ref);
-  free(ba->ring);
+  free(ba->next);
+  free(ba->prev);
+  free(ba->sealed);
+  free(ba->hash);
+  free(ba->parent);
+  free(ba->tokens);
+  free(ba->slot);
   free(ba);
 }
 
@@ -88,7 +203,7 @@ static int valid_id(const pkv_ba_t* ba, int32_t b) { return b >= 0 && b < ba->nu
 int pkv_ba_alloc(pkv_ba_t* ba, int32_t* block) {
   if (!ba || !block) return PKV_ERR_INVALID_ARGUMENT;
   if (ba->count == 0) return PKV_ERR_OUT_OF_BLOCKS;
-  int32_t b = ring_pop_front(ba);
+  int32_t b = q_pop_front(ba);
   ba->ref[b] = 1;
   *block = b;
   return PKV_OK;
@@ -105,7 +220,7 @@ int pkv_ba_incref(pkv_ba_t* ba, int32_t block) {
 int pkv_ba_decref(pkv_ba_t* ba, int32_t block) {
   if (!ba || !valid_id(ba, block)) return PKV_ERR_INVALID_ARGUMENT;
   if (ba->ref[block] <= 0) return PKV_ERR_REFCOUNT;
-  if (--ba->ref[block] == 0) ring_push_back(ba, block);
+  if (--ba->ref[block] == 0) q_push_back(ba, block);
   return PKV_OK;
 }
 
@@ -233,8 +348,64 @@ int pkv_seq_free(pkv_ba_t* ba, const int32_t* table, int32_t nblk) {
   /* undo, newest first: a block that reached zero is the newest push */
   while (--j >= 0) {
     const int32_t b = table[j];
-    if (ba->ref[b] == 0) ring_pop_back(ba);
+    if (ba->ref[b] == 0) q_pop_back(ba);
     ba->ref[b]++;
   }
   return rc;
 }
+
+/* ---- prefix cache ------------------------------------------------------------ */
+
+int pkv_seq_cache_lookup(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens, int32_t* table,
+                         int32_t cap, int32_t* nblk) {
+  if (!ba || !table || !nblk || num_tokens < 0 || cap < 0 || (num_tokens > 0 && !tokens))
+    return PKV_ERR_INVALID_ARGUMENT;
+  const int32_t full = num_tokens / PKV_BLOCK_SIZE;
+  const int32_t limit = full < cap ? full : cap;
+  uint64_t h = 0;
+  int32_t j = 0;
+  for (; j < limit; ++j) {
+    const int32_t* tk = tokens + (int64_t)j * PKV_BLOCK_SIZE;
+    h = pkv_prefix_hash(h, tk);
+    const int32_t b = find_sealed(ba, h, j ? table[j - 1] : -1, tk);
+    if (b < 0 || ba->ref[b] == INT32_MAX) break;
+    if (ba->ref[b] == 0) q_remove(ba, b); /* a cached block back from the free queue */
+    ba->ref[b]++;
+    table[j] = b;
+  }
+  *nblk = j;
+  return PKV_OK;
+}
+
+int pkv_seq_cache_seal(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens,
+                       const int32_t* table, int32_t nblk) {
+  if (!ba || !table || num_tokens < 0 || nblk < 0 || (num_tokens > 0 && !tokens))
+    return PKV_ERR_INVALID_ARGUMENT;
+  const int32_t full = num_tokens / PKV_BLOCK_SIZE;
+  const int32_t n = full < nblk ? full : nblk;
+  int rc = check_table(ba, table, n);
+  if (rc != PKV_OK) return rc;
+  /* verify first, then seal: all or nothing */
+  uint64_t h = 0;
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t* tk = tokens + (int64_t)j * PKV_BLOCK_SIZE;
+    const int32_t b = table[j], parent = j ? table[j - 1] : -1;
+    h = pkv_prefix_hash(h, tk);
+    if (ba->sealed[b] && (ba->hash[b] != h || ba->parent[b] != parent ||
+                          memcmp(ba->tokens + (int64_t)b * PKV_BLOCK_SIZE, tk,
+                                 PKV_BLOCK_SIZE * sizeof(int32_t))))
+      return PKV_ERR_INVALID_ARGUMENT; /* a cached block must keep its contents */
+  }
+  h = 0;
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t* tk = tokens + (int64_t)j * PKV_BLOCK_SIZE;
+    const int32_t b = table[j], parent = j ? table[j - 1] : -1;
+    h = pkv_prefix_hash(h, tk);
+    if (ba->sealed[b]) continue;
+    if (find_sealed(ba, h, parent, tk) >= 0) continue; /* the same content is cached already */
+    seal(ba, b, h, parent, tk);
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_ba_num_cached(const pkv_ba_t* ba) { return ba ? ba->num_sealed : -1; }

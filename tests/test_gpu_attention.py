@@ -234,3 +234,66 @@ def test_contiguous_baseline_equals_paged_bitwise(dtype, hq, hkv, d):
                                 spec.query_start_loc, spec.scale, dtype)
     ok, worst = gp.compare(numerics.to_f64(bc, dtype).reshape(ref.shape), ref, dtype)
     assert ok, worst
+
+
+@pytest.mark.parametrize("prefix,tail_a,tail_b,q_b", [(1000, 37, 50, 1), (10000, 5, 256, 256), (40, 0, 9, 9)])
+def test_prefix_cache_reuse_gives_the_same_attention(prefix, tail_a, tail_b, q_b):
+    """Request B repeats request A's prompt: it takes A's cached blocks, writes only
+    its own tokens, and attends exactly as over its whole prompt."""
+    import torch
+
+    from oracle import attention as oattn
+    from paged_kv_cache_446_amd import ops
+    from paged_kv_cache_446_amd.allocator import BlockAllocator
+
+    gp = _gp()
+    gp.log(f"[prefix-cache] prefix {prefix} tails {tail_a}/{tail_b} q_b {q_b}")
+    nA, nB = prefix + tail_a, prefix + tail_b
+    # sequence 0 = request A, sequence 1 = request B; both start with the shared prefix K/V
+    spec = workloads.make_spec("pcache", (446, 101, prefix), "bf16", 32, 8, 128,
+                               [nA, nB - q_b], [0, q_b], shared_prefix=prefix)
+    rng = np.random.default_rng(prefix)
+    tok_prefix = rng.integers(0, 32000, size=prefix).astype(np.int32)
+    tok_a = np.concatenate([tok_prefix, rng.integers(0, 32000, size=tail_a).astype(np.int32)])
+    tok_b = np.concatenate([tok_prefix, rng.integers(0, 32000, size=tail_b).astype(np.int32)])
+    nblocks = 2 * (-(-nB // 16)) + 8
+    alloc = BlockAllocator(nblocks, free_order=np.random.default_rng(3).permutation(nblocks).astype(np.int32))
+    kp = torch.zeros(nblocks * 8 * 16 * 128, dtype=torch.int16, device="cuda:0")
+    vp = torch.zeros_like(kp)
+    cache = ops.PagedCache(kp, vp, 8, 128, dtype="bf16")
+    cap = -(-nB // 16) + 1
+
+    def write(seq, t0, t1, slots):
+        k, v = spec.kv_bits(seq, t0, t1)
+        ops.kv_cache_write(cache, gp.dev_bits(k, "bf16"), gp.dev_bits(v, "bf16"),
+                           torch.from_numpy(np.ascontiguousarray(slots)).to("cuda:0"))
+
+    # request A: nothing cached yet
+    ta = alloc.new_table(cap)
+    assert alloc.cache_lookup(tok_a, ta) == 0
+    nb_a, _, slots_a, _ = alloc.append_slots(ta, 0, 0, nA)
+    write(0, 0, nA, slots_a)
+    alloc.cache_seal(tok_a, ta, nb_a)
+    alloc.free_seq(ta, nb_a)  # A finishes; its full blocks stay cached
+    # request B: the cached full blocks of the shared prompt, then its own tokens
+    tb = alloc.new_table(cap)
+    hit = alloc.cache_lookup(tok_b, tb)
+    assert hit == prefix // 16
+    nb_b, _, slots_b, _ = alloc.append_slots(tb, hit, hit * 16, nB - hit * 16)
+    write(1, hit * 16, nB, slots_b)
+    alloc.cache_seal(tok_b, tb, nb_b)
+    torch.cuda.synchronize()
+
+    q = gp.dev_bits(spec.q_bits(1), "bf16")
+    out = torch.zeros_like(q)
+    ws = torch.empty(ops.workspace_bytes(1, q_b, nB, 32, 128), dtype=torch.uint8, device="cuda:0")
+    ops.paged_attention(cache, out, q, torch.from_numpy(tb[None, :nb_b].copy()).to("cuda:0"),
+                        torch.tensor([nB], dtype=torch.int32, device="cuda:0"),
+                        torch.tensor([0, q_b], dtype=torch.int32, device="cuda:0"),
+                        num_q_heads=32, max_q_len=q_b, max_seq_len=nB, scale=spec.scale, workspace=ws)
+    torch.cuda.synchronize()
+    K, V = (numerics.to_f64(x, "bf16") for x in spec.kv_bits(1))
+    ref = oattn.attend(numerics.to_f64(spec.q_bits(1), "bf16"), K, V, spec.scale)
+    got = numerics.to_f64(gp.host_bits(out, "bf16"), "bf16").reshape(ref.shape)
+    ok, worst = gp.compare(got, ref, "bf16")
+    assert ok, worst
