@@ -257,6 +257,8 @@ def main():
                          "contiguous: each sequence in one run of consecutive blocks")
     ap.add_argument("--kernel", default="paged", choices=["paged", "contiguous"],
                     help="contiguous: the table-free baseline (needs --placement contiguous)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a kernel of known size for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -387,6 +389,29 @@ def main():
     log(f"{K} steps: {ms_step * 1e3:.1f} us/step (GPU events), wall {wall / K * 1e6:.1f} us/step, "
         f"attention {attn_avg * 1e3:.1f} us (min {min(attn_ms) * 1e3:.1f})")
 
+    graph_ms = None
+    if args.graph:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            step()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=gs):
+                step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record()
+        for _ in range(K):
+            g.replay()
+        gb.record()
+        torch.cuda.synchronize()
+        graph_ms = ga.elapsed_time(gb) / K
+        log(f"graph replay: {graph_ms * 1e3:.1f} us/step (eager {ms_step * 1e3:.1f})")
+
     kv_bytes, attn_bytes = algorithmic_bytes(spec)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = attn_bytes / (attn_avg * 1e-3) / 1e9
@@ -421,6 +446,7 @@ def main():
         "context_tokens_per_s": round(int(spec.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "host_alloc_us": round(host_alloc_us, 1),
+        "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
         "roofline": {
             "kernel": ("contiguous_attention" if args.kernel == "contiguous" else "paged_attention") +
                       " (plan + decode partition kernel + partition merge)",
