@@ -34,6 +34,7 @@ WORKLOAD_NAMES = {
     "c3": "Llama-3-8B-shaped GQA decode: 256 seqs, context log-uniform [64,8192], 32q/8kv heads, head_dim 128, bf16",
     "c4": "shared-prefix parallel sampling: 64 seqs share a 10000-token prefix + U[0,256] private tails, CoW, 32q/8kv, bf16",
     "c5": "mixed chunked-prefill + decode: 16 chunks q U[16,512] over context U[0,32768] + 128 decodes U[64,8192], 32q/8kv, bf16",
+    "verify": "speculative-decoding verify: 256 seqs, context log-uniform [64,8192], k+1=5 query tokens each, 32q/8kv heads, head_dim 128, bf16",
     "prefix-cache": "repeated 10000-token prompt + 256 new tokens (second request), 32q/8kv heads, head_dim 128, bf16",
 }
 
@@ -449,7 +450,7 @@ def main():
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
         "roofline": {
             "kernel": ("contiguous_attention" if args.kernel == "contiguous" else "paged_attention") +
-                      " (plan + decode partition kernel + partition merge)",
+                      " (plan + partitioned decode kernel + partition merge)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

@@ -19,7 +19,10 @@
 // S^T result already in place.
 //
 // Decode splits the context of a sequence into partitions of kPartBlocks
-// blocks (1024 tokens).  One workgroup per (sequence, partition, KV head):
+// blocks (1024 tokens).  Short chunks (a few query tokens, e.g. the k+1
+// tokens that verify a speculative draft) take the same kernel with their
+// q_len * G columns in one or two column tiles, so K/V are read once per row.
+// One workgroup per (sequence, partition, KV head):
 // its four wavefronts take every fourth block, streaming K/V tiles with
 // non-temporal loads (each tile is read once), merge through LDS, and a
 // second kernel merges the partitions of long sequences with the log-sum-exp
@@ -35,223 +38,309 @@
 namespace pkv {
 
 constexpr int kPartBlocks = 64;  // blocks per decode partition (1024 tokens)
-constexpr int kPerWave = kPartBlocks / kWaves;  // blocks of a partition per wavefront
-constexpr int kXcds = 8;         // accelerator complex dies of an MI355X
-static_assert(kPerWave <= 64, "one block-table entry per lane");
-
 
 // ---------------------------------------------------------------------------
-// Decode: a 1-D grid over (sequence, partition, KV head), 4 wavefronts each.
+// Decode and short chunks: a 1-D grid over (item, KV head), 4 wavefronts each.
+// A row of q_len query tokens has q_len * G (token, head) columns per KV head;
+// the kernel instantiation with CT column tiles takes the rows with
+// (CT-1)*16 < q_len * G <= CT*16, so a decode row (q_len = 1) fills G columns
+// of one tile and a speculative-decoding verify row of k+1 tokens fills
+// (k+1) * G columns (blog page, advanced features, speculative decoding).
 // ---------------------------------------------------------------------------
 
-// Waves per SIMD the register allocation must allow: three for the 16-bit
-// types up to head_dim 128 (enough K/V bytes in flight per CU), otherwise
-// whatever the kernel needs.
-template <class DT, int D>
+// Waves per SIMD the register allocation must allow: three for one column
+// tile of a 16-bit type up to head_dim 128 (enough K/V bytes in flight per
+// CU), two for two tiles, otherwise whatever the kernel needs.
+template <class DT, int D, int CT>
 constexpr int decode_occupancy() {
-  return (DT::kBytes == 2 && D <= 128) ? 3 : 1;
+  return (DT::kBytes == 2 && D <= 128) ? (CT == 1 ? 3 : 2) : 1;
 }
 
-// Work lists of one call, written by decode_plan_kernel: the live decode items
-// (sequence, partition) in sequence order, and the sequences whose partitions
-// need merging.  plan[0] = number of items, plan[1] = number of merges.
-struct DecodePlan {
-  int32_t* counts;
-  int2* items;     // [num_seqs * max_parts]
-  int32_t* merge;  // [num_seqs]
+// Work lists of one call, written by decode_plan_kernel.  An item is
+// (sequence, partition, first block, end block); the lists hold the items of
+// one-tile rows, then (from offset cap) those of two-tile rows, each in
+// sequence order.  Sequences split over several partitions are listed in merge
+// and own workspace rows from base[s]: row base[s] + (p * q_len + t) * Hq + head
+// holds partition p's result for query token t.
+// One merge: the output query row, the partition count, the workspace row of
+// (partition 0, this token, head 0) and the rows between partitions.
+struct MergeEntry {
+  int32_t qrow, nparts, unused0, unused1;
+  int64_t row0, pstride;
 };
 
-// One workgroup of 1024 threads; thread t owns sequences [t*k, t*k + k).
-// A decode row (q_len = 1) of a sequence with n > 0 tokens has one item per
-// 1024-token partition; an empty sequence has one item (its zero output).
+struct DecodePlan {
+  int32_t* counts;    // [0] one-tile items, [1] merges, [2] two-tile items;
+                      // nullptr: no plan, every row is one item (single-partition batches)
+  int4* items;        // [2 * cap]
+  MergeEntry* merge;  // [num_seqs * 32]
+  int64_t* base;      // [num_seqs]
+  int num_seqs;
+  int cap;            // num_seqs * max_parts
+};
+
+// Blocks per partition of a row: 1024 tokens for decode rows; a multi-token row
+// uses 1024 << shift, with the shift the plan chose so that the split rows fit
+// the workspace.
+__device__ __forceinline__ int part_blocks(int q_len, int shift) {
+  return q_len > 1 ? kPartBlocks << shift : kPartBlocks;
+}
+
+// Column-tile class of a row: 1 or 2, or 0 for rows left to the prefill kernels
+// (and rows with no query token, or more than the call's max_q_len).
+__device__ __forceinline__ int row_class(int q_len, int max_q, int G, int max_cols) {
+  const int64_t cols = (int64_t)q_len * G;
+  if (q_len < 1 || q_len > max_q || cols > max_cols) return 0;
+  return cols <= 16 ? 1 : 2;
+}
+
+// One workgroup of 1024 threads; thread t owns sequences [t*k, t*k + k).  A
+// small row of a sequence with n > 0 tokens has one item per partition; an
+// empty sequence has one item (its zero output).  A split row has one merge
+// entry per query token.  budget: workspace rows for split rows
+// (each row is head_dim floats).  The partition shift starts at 0 and grows
+// until the split rows fit; this terminates, since once a partition spans
+// max_parts * 1024 tokens no multi-token row is split, and decode rows alone
+// need at most num_seqs * max_parts * hq rows.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int num_seqs,
-    int bt_stride, int max_parts, int32_t* __restrict__ counts, int2* __restrict__ items,
-    int32_t* __restrict__ merge) {
-  __shared__ int sm_tot[2][1024 / kWave];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int bt_stride, int max_parts, int max_q, int G, int max_cols, int hq, long long budget,
+    DecodePlan plan) {
+  __shared__ int sm_tot[3][1024 / kWave];
+  __shared__ long long sm_rows[1024 / kWave];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nwaves = blockDim.x / kWave;
   const int k = (num_seqs + blockDim.x - 1) / blockDim.x;
   const int s0 = tid * k;
-  int nit = 0, nmg = 0;
-  for (int j = 0; j < k; ++j) {
-    const int s = s0 + j;
-    if (s >= num_seqs) break;
-    if (qsl[s + 1] - qsl[s] != 1) continue;
-    const int n = seq_lens[s];
-    const int nb = n > 0 ? min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks)) : 0;
-    const int np = n > 0 ? (nb + kPartBlocks - 1) / kPartBlocks : 1;
-    nit += np;
-    nmg += np > 1;
-  }
-  // exclusive prefix of (nit, nmg) over the workgroup: wave scan, then wave totals
-  int xi = nit, xm = nmg;
+  auto blocks = [&](int n) {
+    return n > 0 ? min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks)) : 0;
+  };
+  int shift = 0, n1, n2, nmg, x1, x2, xm;
+  long long nrow, xr, trow;
+  for (;; ++shift) {
+    n1 = n2 = nmg = 0;
+    nrow = 0;
+    for (int j = 0; j < k; ++j) {
+      const int s = s0 + j;
+      if (s >= num_seqs) break;
+      const int q_len = qsl[s + 1] - qsl[s];
+      const int cls = row_class(q_len, max_q, G, max_cols);
+      if (!cls) continue;
+      const int n = seq_lens[s], pb = part_blocks(q_len, shift);
+      const int np = n > 0 ? (blocks(n) + pb - 1) / pb : 1;
+      (cls == 1 ? n1 : n2) += np;
+      if (np > 1) {
+        nmg += q_len;
+        nrow += (long long)np * q_len * hq;
+      }
+    }
+    // inclusive prefix of (n1, n2, nmg, nrow) within the wavefront, then wave totals
+    x1 = n1, x2 = n2, xm = nmg, xr = nrow;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int yi = __shfl_up(xi, off), ym = __shfl_up(xm, off);
-    if (lane >= off) {
-      xi += yi;
-      xm += ym;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y1 = __shfl_up(x1, off), y2 = __shfl_up(x2, off), ym = __shfl_up(xm, off);
+      const long long yr = __shfl_up(xr, off);
+      if (lane >= off) {
+        x1 += y1;
+        x2 += y2;
+        xm += ym;
+        xr += yr;
+      }
     }
+    if (lane == kWave - 1) {
+      sm_tot[0][w] = x1;
+      sm_tot[1][w] = x2;
+      sm_tot[2][w] = xm;
+      sm_rows[w] = xr;
+    }
+    __syncthreads();
+    trow = 0;
+    for (int ww = 0; ww < nwaves; ++ww) trow += sm_rows[ww];
+    if (trow <= budget || (kPartBlocks << shift) >= max_parts * kPartBlocks) break;
+    __syncthreads();  // every wave has read the totals before the next round writes them
   }
-  if (lane == kWave - 1) {
-    sm_tot[0][w] = xi;
-    sm_tot[1][w] = xm;
-  }
-  __syncthreads();
-  int bi = 0, bm = 0, ti = 0, tm = 0;
-  for (int ww = 0; ww < (int)(blockDim.x / kWave); ++ww) {
+  int b1 = 0, b2 = 0, bm = 0, t1 = 0, t2 = 0, tm = 0;
+  long long br = 0;
+  for (int ww = 0; ww < nwaves; ++ww) {
     if (ww < w) {
-      bi += sm_tot[0][ww];
-      bm += sm_tot[1][ww];
+      b1 += sm_tot[0][ww];
+      b2 += sm_tot[1][ww];
+      bm += sm_tot[2][ww];
+      br += sm_rows[ww];
     }
-    ti += sm_tot[0][ww];
-    tm += sm_tot[1][ww];
+    t1 += sm_tot[0][ww];
+    t2 += sm_tot[1][ww];
+    tm += sm_tot[2][ww];
   }
-  int pi = bi + xi - nit, pm = bm + xm - nmg;
+  int p1 = b1 + x1 - n1, p2 = b2 + x2 - n2, pm = bm + xm - nmg;
+  long long pr = br + xr - nrow;
   for (int j = 0; j < k; ++j) {
     const int s = s0 + j;
     if (s >= num_seqs) break;
-    if (qsl[s + 1] - qsl[s] != 1) continue;
-    const int n = seq_lens[s];
-    const int nb = n > 0 ? min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks)) : 0;
-    const int np = n > 0 ? (nb + kPartBlocks - 1) / kPartBlocks : 1;
-    for (int p = 0; p < np; ++p) items[pi + p] = int2{s, p};
-    pi += np;
-    if (np > 1) merge[pm++] = s;
+    const int q_len = qsl[s + 1] - qsl[s];
+    const int cls = row_class(q_len, max_q, G, max_cols);
+    if (!cls) continue;
+    const int n = seq_lens[s], nb = blocks(n), pb = part_blocks(q_len, shift);
+    const int np = n > 0 ? (nb + pb - 1) / pb : 1;
+    int4* dst = plan.items + (cls == 1 ? (int64_t)p1 : (int64_t)plan.cap + p2);
+    for (int p = 0; p < np; ++p) dst[p] = int4{s, p, p * pb, min(nb, (p + 1) * pb)};
+    (cls == 1 ? p1 : p2) += np;
+    if (np > 1) {
+      for (int t = 0; t < q_len; ++t)
+        plan.merge[pm++] =
+            MergeEntry{qsl[s] + t, np, 0, 0, pr + (long long)t * hq, (long long)q_len * hq};
+      plan.base[s] = pr;
+      pr += (long long)np * q_len * hq;
+    }
   }
   if (tid == 0) {
-    counts[0] = ti;
-    counts[1] = tm;
+    plan.counts[0] = t1;
+    plan.counts[1] = tm;
+    plan.counts[2] = t2;
   }
 }
 
-// Workgroup id -> index into a list of `live` work units.  Dispatch deals
-// consecutive ids round-robin over the XCDs; unit j = (id % 8) * C + id / 8
-// with C = ceil(live / 8) gives every XCD one contiguous run of units.  Ids
-// whose unit is past the list (the grid is sized for the worst case) come
-// last in dispatch order and return at once; returns -1 for them.
-__device__ __forceinline__ int xcd_unit(int id, int live) {
-  const int per = (live + kXcds - 1) / kXcds;
-  const int r = id / kXcds;
-  if (r >= per) return -1;
-  const int j = (id % kXcds) * per + r;
-  return j < live ? j : -1;
-}
-
-template <class DT, int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_occupancy<DT, D>())))
+template <class DT, int D, int G, int CT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_occupancy<DT, D, CT>())))
 void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
                    const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
                    const int32_t* __restrict__ bt, int bt_stride,
                    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
-                   int num_kv_heads, float scale_log2, int max_parts,
+                   int num_kv_heads, float scale_log2, int max_parts, int max_q,
                    float* __restrict__ ws_o, float* __restrict__ ws_ml, DecodePlan plan,
                    int contiguous) {
   typedef Geo<DT, D> Gm;
-  const int j = xcd_unit(blockIdx.x, plan.counts[0] * num_kv_heads);
+  const int live = (plan.counts ? plan.counts[CT == 1 ? 0 : 2] : plan.num_seqs) * num_kv_heads;
+  const int j = xcd_unit(blockIdx.x, live);
   if (j < 0) return;
   const int h = j % num_kv_heads;
-  const int2 item = plan.items[j / num_kv_heads];
-  const int s = item.x, part = item.y;
+  const int4 item = plan.counts ? plan.items[(CT == 1 ? 0 : (int64_t)plan.cap) + j / num_kv_heads]
+                                : int4{j / num_kv_heads, 0, 0, kPartBlocks};
+  const int s = item.x, part = item.y, b0 = item.z;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
-  const int b0 = part * kPartBlocks;
   const int32_t* btr = bt + (int64_t)s * bt_stride;
-  // block-table entries of this wavefront's blocks b0 + w + 4i, one per lane,
-  // loaded alongside the sequence metadata (bounded by the table width only).
+  // block-table entries of this wavefront's first blocks b0 + w + 4i, one per lane,
+  // loaded alongside the sequence metadata (bounded by the item and the table width).
   // Contiguous storage (the baseline without paging): bt[s] is the sequence's
   // first block and block i is bt[s] + i.
-  int btv = 0;
-  {
-    const int bi = b0 + w + kWaves * lane;
-    if (lane < kPerWave && bi < bt_stride) btv = contiguous ? bt[s] + bi : btr[bi];
-  }
-  const int qb = qsl[s];
-  if (qsl[s + 1] - qb != 1) return;
+  auto table = [&](int i) {  // entry of this wavefront's block i (relative), or 0
+    const int bi = b0 + w + kWaves * i;
+    return (bi < item.w && bi < bt_stride) ? (contiguous ? bt[s] + bi : btr[bi]) : 0;
+  };
+  int btv = table(lane);
+  const int qb = qsl[s], q_len = qsl[s + 1] - qb;
   const int n = seq_lens[s];
+  const int cols = q_len * G;
+  if (q_len < 1 || q_len > max_q || cols > CT * 16 || cols <= (CT - 1) * 16) return;  // not ours
   const int hq = num_kv_heads * G;
   if (n <= 0) {
     if (part == 0)
-      for (int e = threadIdx.x; e < G * D; e += blockDim.x)
-        store_elem<DT>(out, ((int64_t)qb * hq + h * G) * D + e, 0.f);
+      for (int e = threadIdx.x; e < cols * D; e += blockDim.x)
+        store_elem<DT>(out, ((int64_t)(qb + e / D / G) * hq + h * G + (e / D) % G) * D + e % D, 0.f);
     return;
   }
   // a sequence longer than the bounds the host passed is cut at them (never read past them)
   const int nblocks = min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks));
-  if (b0 >= nblocks) return;
-  const int b1 = min(nblocks, b0 + kPartBlocks);
-  const int nparts = (nblocks + kPartBlocks - 1) / kPartBlocks;
+  const int b1 = min(nblocks, item.w);
+  if (b0 >= b1) return;
+  const bool split = b0 > 0 || b1 < nblocks;  // the row has other partitions
+  const int ctx = n - q_len;
   const int g = lane >> 4, c = lane & 15;
 
-  WaveState<DT, D> st;
-  load_q<DT, D>(st, q + ((int64_t)qb * hq + h * G + (c < G ? c : 0)) * D, c < G, g);
+  WaveState<DT, D> st[CT];
+  int lim[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = ct * 16 + c, tq = col / G;
+    const bool valid = col < cols;
+    lim[ct] = valid ? ctx + tq : -1;  // a column past the row sees nothing
+    load_q<DT, D>(st[ct], q + ((int64_t)(qb + (valid ? tq : 0)) * hq + h * G + col % G) * D, valid, g);
+  }
 
   const int64_t head_off = (int64_t)h * Gm::kTile;
   const int64_t blk_elems = (int64_t)num_kv_heads * Gm::kTile;
   const int nw = (b0 + w < b1) ? (b1 - b0 - w + kWaves - 1) / kWaves : 0;  // blocks of this wave
-  auto fetch = [&](TileBuf<DT, D>& tb, int i) {
-    const int64_t phys = __builtin_amdgcn_readlane(btv, i);
-    load_tile<DT, D, true>(kp + phys * blk_elems + head_off, vp + phys * blk_elems + head_off,
-                           tb.k, tb.v, lane);
-  };
-  auto consume = [&](TileBuf<DT, D>& tb, int i) {
-    attend_block<DT, D>(st, tb.k, tb.v, (b0 + w + kWaves * i) * kBlock, n, n - 1, scale_log2, g);
-  };
-  // two register buffers, both in flight: each iteration uses a tile and refills its buffer
-  // two tiles ahead.  The prologue waits once for Q and the first two tiles; after that
-  // every wait covers exactly the tile about to be used, and the refill is kept after the
-  // use (a hoisted load would need fresh registers and a copy at the loop edge).
-  TileBuf<DT, D> A, B;
-  if (nw > 0) fetch(A, 0);
-  if (nw > 1) fetch(B, 1);
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
-  int i = 0;
-  for (; i + 3 < nw; i += 2) {
-    consume(A, i);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(A, i + 2);
-    consume(B, i + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(B, i + 3);
+  for (int i0 = 0; i0 < nw; i0 += kWave) {
+    if (i0 > 0) btv = table(i0 + lane);
+    const int cnt = min(kWave, nw - i0);
+    auto fetch = [&](TileBuf<DT, D>& tb, int i) {
+      const int64_t phys = __builtin_amdgcn_readlane(btv, i);
+      load_tile<DT, D, true>(kp + phys * blk_elems + head_off, vp + phys * blk_elems + head_off,
+                             tb.k, tb.v, lane);
+    };
+    auto consume = [&](TileBuf<DT, D>& tb, int i) {
+      const int tok0 = (b0 + w + kWaves * (i0 + i)) * kBlock;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        attend_block<DT, D>(st[ct], tb.k, tb.v, tok0, n, lim[ct], scale_log2, g);
+    };
+    // two register buffers, both in flight: each iteration uses a tile and refills its
+    // buffer two tiles ahead.  The prologue waits once for Q and the first two tiles;
+    // after that every wait covers exactly the tile about to be used, and the refill is
+    // kept after the use (a hoisted load would need fresh registers and a copy at the
+    // loop edge).
+    TileBuf<DT, D> A, B;
+    fetch(A, 0);
+    if (cnt > 1) fetch(B, 1);
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+    int i = 0;
+    for (; i + 3 < cnt; i += 2) {
+      consume(A, i);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(A, i + 2);
+      consume(B, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(B, i + 3);
+    }
+    if (i < cnt) consume(A, i);
+    if (i + 2 < cnt) fetch(A, i + 2);
+    if (i + 1 < cnt) consume(B, i + 1);
+    if (i + 2 < cnt) consume(A, i + 2);
   }
-  if (i < nw) consume(A, i);
-  if (i + 2 < nw) fetch(A, i + 2);
-  if (i + 1 < nw) consume(B, i + 1);
-  if (i + 2 < nw) consume(A, i + 2);
 
   // merge the four wavefronts through LDS
-  __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
-  __shared__ float sm_o[kWaves][G][D];
-  float lsum = st.l + shfl_xor(st.l, 16);
-  lsum += shfl_xor(lsum, 32);
-  if (g == 0) {
-    sm_m[w][c] = st.m;
-    sm_l[w][c] = lsum;
-  }
-  if (c < G) {
+  __shared__ float sm_m[kWaves][CT * 16], sm_l[kWaves][CT * 16];
+  __shared__ float sm_o[kWaves][CT * 16][D];
 #pragma unroll
-    for (int nn = 0; nn < Gm::kN; ++nn)
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = ct * 16 + c;
+    float lsum = st[ct].l + shfl_xor(st[ct].l, 16);
+    lsum += shfl_xor(lsum, 32);
+    if (g == 0) {
+      sm_m[w][col] = st[ct].m;
+      sm_l[w][col] = lsum;
+    }
+    if (col < cols) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[w][c][nn * 16 + 4 * g + i] = st.acc[nn][i];
+      for (int nn = 0; nn < Gm::kN; ++nn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm_o[w][col][nn * 16 + 4 * g + r] = st[ct].acc[nn][r];
+    }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int cc = e / D, d = e - cc * D;
-    float M = sm_m[0][cc];
+  const int64_t wrow0 = split ? plan.base[s] + (int64_t)part * q_len * hq : 0;
+  for (int e = threadIdx.x; e < cols * D; e += blockDim.x) {
+    const int col = e / D, d = e - col * D;
+    float M = sm_m[0][col];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][cc]);
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][col]);
+    // a partition that starts inside a multi-token row hides it from the row's
+    // earlier tokens: such a column has M = -inf and leaves (o, m, l) = (0, -inf, 0)
+    const float Mu = M == -INFINITY ? 0.f : M;
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fast_exp2(sm_m[ww][cc] - M);  // wavefronts without blocks: -inf -> 0
-      num += f * sm_o[ww][cc][d];
-      den += f * sm_l[ww][cc];
+      const float f = fast_exp2(sm_m[ww][col] - Mu);  // wavefronts without blocks: -inf -> 0
+      num += f * sm_o[ww][col][d];
+      den += f * sm_l[ww][col];
     }
-    if (nparts == 1) {
-      store_elem<DT>(out, ((int64_t)qb * hq + h * G + cc) * D + d, num / den);
+    const float o = den > 0.f ? num / den : 0.f;
+    const int64_t qrow = (int64_t)(col / G) * hq + h * G + col % G;  // within the row's tokens
+    if (!split) {
+      store_elem<DT>(out, ((int64_t)qb * hq + qrow) * D + d, o);
     } else {
-      const int64_t idx = ((int64_t)s * max_parts + part) * hq + h * G + cc;
-      ws_o[idx * D + d] = num / den;
+      const int64_t idx = wrow0 + qrow;
+      ws_o[idx * D + d] = o;
       if (d == 0) {
         ws_ml[2 * idx] = M;
         ws_ml[2 * idx + 1] = den;
@@ -260,59 +349,56 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
   }
 }
 
-// Merge of decode partitions, one workgroup per (sequence, KV head):
+// Merge of the partitions of split rows, one workgroup per (merge entry = split
+// sequence and query token, KV head):
 //   o = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-// Every thread owns outputs of one query head and loads the (m, l, o) of all
-// partitions at once, kMergeBatch partitions per round, so a merge costs one
-// memory round trip after the sequence metadata (C3-like contexts: one round).
+// A thread owns four consecutive outputs of one query head and loads the (m, l)
+// pair and the four partial outputs of kMergeBatch partitions at once, so a
+// merge costs one memory round trip after its entry (contexts up to 8192
+// tokens: one round).
 constexpr int kMergeBatch = 8;
 
 template <class DT, int D, int G>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     typename DT::T* __restrict__ out, const float* __restrict__ ws_o,
-    const float* __restrict__ ws_ml, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ qsl, int num_kv_heads, int max_parts, int bt_stride,
-    DecodePlan plan) {
+    const float* __restrict__ ws_ml, int num_kv_heads, DecodePlan plan) {
   const int j = xcd_unit(blockIdx.x, plan.counts[1] * num_kv_heads);
   if (j < 0) return;
-  const int s = plan.merge[j / num_kv_heads], h = j % num_kv_heads;
-  const int qb = qsl[s];
-  if (qsl[s + 1] - qb != 1) return;
-  const int n = seq_lens[s];
-  const int nblocks = min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks));
-  const int nparts = (nblocks + kPartBlocks - 1) / kPartBlocks;
-  if (nparts <= 1) return;
+  const MergeEntry me = plan.merge[j / num_kv_heads];
+  const int h = j % num_kv_heads;
   const int hq = num_kv_heads * G;
-  const int64_t base = (int64_t)s * max_parts * hq + h * G;  // (partition 0, head h*G)
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int cc = e / D, d = e - cc * D;
-    const int64_t row0 = base + cc;  // this head's row in partition 0; + p*hq for partition p
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int p0 = 0; p0 < nparts; p0 += kMergeBatch) {
-      float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch];
+  constexpr int kQuads = D / 4;
+  for (int u = threadIdx.x; u < G * kQuads; u += blockDim.x) {
+    const int cc = u / kQuads, d = (u - cc * kQuads) * 4;
+    const int64_t row0 = me.row0 + h * G + cc;  // partition 0; + p * pstride for partition p
+    float M = -INFINITY, den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < me.nparts; p0 += kMergeBatch) {
+      float2 ml[kMergeBatch];
+      f32x4 op[kMergeBatch];
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) {
-        const int p = min(p0 + k, nparts - 1);  // past the end: re-read the last (weight 0)
-        const int64_t row = row0 + (int64_t)p * hq;
-        mp[k] = ws_ml[2 * row];
-        lp[k] = ws_ml[2 * row + 1];
-        op[k] = ws_o[row * D + d];
+        const int p = min(p0 + k, me.nparts - 1);  // past the end: re-read the last (weight 0)
+        const int64_t row = row0 + p * me.pstride;
+        ml[k] = *(const float2*)(ws_ml + 2 * row);
+        op[k] = *(const f32x4*)(ws_o + row * D + d);
       }
       float bm = M;
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, mp[k]);
+      for (int k = 0; k < kMergeBatch; ++k) bm = fmaxf(bm, ml[k].x);
       const float f0 = fast_exp2(M - bm);  // M = -inf on the first round: 0
       num *= f0;
       den *= f0;
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) {
-        const float f = p0 + k < nparts ? fast_exp2(mp[k] - bm) * lp[k] : 0.f;
+        // hidden partitions (m = -inf, l = 0) weigh 0; partition 0 is never hidden
+        const float f = p0 + k < me.nparts ? fast_exp2(ml[k].x - bm) * ml[k].y : 0.f;
         num += f * op[k];
         den += f;
       }
       M = bm;
     }
-    store_elem<DT>(out, ((int64_t)qb * hq + h * G + cc) * D + d, num / den);
+    store4<DT>(out, ((int64_t)me.qrow * hq + h * G + cc) * D + d, num / den);
   }
 }
 
@@ -320,29 +406,65 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 // host side
 // ---------------------------------------------------------------------------
 
+static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// counts, two item lists, merge entries (up to 32 query tokens per sequence), row bases
+static int64_t decode_plan_bytes(int64_t num_seqs, int64_t max_parts) {
+  return round256(256 + 2 * num_seqs * max_parts * (int64_t)sizeof(int4)) +
+         round256(num_seqs * 32 * (int64_t)sizeof(MergeEntry)) + round256(num_seqs * 8);
+}
+
+// Workspace rows (head_dim floats each) for the partial results of split rows:
+// twice what a decode-only batch can need, so that short multi-token rows split
+// too (the plan enlarges their partitions when they would not fit).
+static int64_t split_rows(int64_t num_seqs, int64_t max_parts, int64_t num_q_heads) {
+  return 2 * num_seqs * max_parts * num_q_heads;
+}
+
+template <class DT, int D, int G, int CT>
+static void launch_ct(const AttnArgs& a, const DecodePlan& plan) {
+  typedef typename DT::T T;
+  // grids sized for every sequence in every partition; the plan's counts cut them short
+  const int64_t units = (int64_t)a.num_kv_heads * a.max_parts * a.num_seqs;
+  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((decode_kernel<DT, D, G, CT>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                     (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
+                     a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, a.max_parts, a.max_q_len,
+                     a.ws_o, a.ws_ml, plan, a.contiguous);
+}
 
 template <class DT, int D, int G>
 static int launch(const AttnArgs& a) {
   typedef typename DT::T T;
-  dim3 blk(256);
+  constexpr int kMaxCols = (DT::kBytes == 2 && D <= 128) ? 32 : 16;
   DecodePlan plan;
-  plan.counts = (int32_t*)a.ws_plan;
-  plan.items = (int2*)((char*)a.ws_plan + 256);
-  plan.merge = (int32_t*)((char*)plan.items + (size_t)a.num_seqs * a.max_parts * sizeof(int2));
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
-                     a.num_seqs, a.bt_stride, a.max_parts, plan.counts, plan.items, plan.merge);
-  // grids sized for every sequence in every partition; the plan's counts cut them short
-  const int64_t units = (int64_t)a.num_kv_heads * a.max_parts * a.num_seqs;
-  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((decode_kernel<DT, D, G>), dim3((unsigned)grid), blk, 0, a.stream,
-                     (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
-                     a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, a.max_parts, a.ws_o,
-                     a.ws_ml, plan, a.contiguous);
+  plan.num_seqs = a.num_seqs;
+  plan.cap = a.num_seqs * a.max_parts;
+  plan.counts = nullptr;
+  plan.items = nullptr;
+  plan.merge = nullptr;
+  plan.base = nullptr;
   if (a.max_parts > 1) {
-    const int64_t mgrid = ((int64_t)a.num_seqs * a.num_kv_heads + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((decode_merge_kernel<DT, D, G>), dim3((unsigned)mgrid), blk, 0, a.stream,
-                       (T*)a.out, a.ws_o, a.ws_ml, a.seq_lens, a.qsl, a.num_kv_heads,
-                       a.max_parts, a.bt_stride, plan);
+    // sequences may span several partitions: list the live (sequence, partition) items
+    plan.counts = (int32_t*)a.ws_plan;
+    plan.items = (int4*)((char*)a.ws_plan + 256);
+    char* mp = (char*)a.ws_plan + round256(256 + 2 * (int64_t)plan.cap * sizeof(int4));
+    plan.merge = (MergeEntry*)mp;
+    plan.base = (int64_t*)(mp + round256((int64_t)a.num_seqs * 32 * sizeof(MergeEntry)));
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
+                       a.num_seqs, a.bt_stride, a.max_parts, a.max_q_len, G, kMaxCols,
+                       a.num_kv_heads * G,
+                       (long long)split_rows(a.num_seqs, a.max_parts, a.num_kv_heads * G), plan);
+  }
+  launch_ct<DT, D, G, 1>(a, plan);
+  if constexpr (kMaxCols > 16)
+    if ((int64_t)a.max_q_len * G > 16) launch_ct<DT, D, G, 2>(a, plan);
+  if (a.max_parts > 1) {
+    // merge entries: at most one per query token of the rows this kernel takes
+    const int64_t qmax = a.max_q_len < kMaxCols / G ? a.max_q_len : kMaxCols / G;
+    const int64_t mgrid = ((int64_t)a.num_seqs * qmax * a.num_kv_heads + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((decode_merge_kernel<DT, D, G>), dim3((unsigned)mgrid), dim3(256), 0,
+                       a.stream, (T*)a.out, a.ws_o, a.ws_ml, a.num_kv_heads, plan);
   }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -370,12 +492,6 @@ static int dispatch_d(const AttnArgs& a, int D, int G) {
   return PKV_ERR_UNSUPPORTED;
 }
 
-static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
-
-static int64_t decode_plan_bytes(int64_t num_seqs, int64_t max_parts) {
-  return round256(256 + num_seqs * max_parts * (int64_t)sizeof(int2) + num_seqs * 4);
-}
-
 static int64_t max_partitions(int32_t max_seq_len) {
   const int64_t nb = ((int64_t)max_seq_len + kBlock - 1) / kBlock;
   const int64_t p = (nb + kPartBlocks - 1) / kPartBlocks;
@@ -392,8 +508,8 @@ extern "C" size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t 
   if (num_seqs < 0 || num_q_tokens < 0 || max_seq_len < 0 || num_q_heads <= 0 || head_dim <= 0)
     return 0;
   const int64_t parts = max_partitions(max_seq_len);
-  const int64_t rows = (int64_t)num_seqs * parts * num_q_heads;
-  // decode (m, l) pairs, decode partition outputs, prefill work list, decode plan; each
+  const int64_t rows = split_rows(num_seqs, parts, num_q_heads);
+  // split rows' (m, l) pairs and partition outputs, prefill work list, decode plan; each
   // section 256-byte aligned
   return (size_t)(round256(rows * 2 * 4) + round256(rows * (int64_t)head_dim * 4) +
                   round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads)) +
@@ -423,8 +539,9 @@ static int attention_impl(const pkv_cache_t* cache, int32_t layer, void* out, co
   const int G = num_q_heads / cache->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
   if (cache->dtype == PKV_F32 && cache->head_dim == 256) return PKV_ERR_UNSUPPORTED;
-  // the decode grid (padded to whole XCD rounds) must fit its limit
-  if ((int64_t)num_seqs * cache->num_kv_heads * max_partitions(max_seq_len) + kXcds > 0x7fffffff)
+  // the decode and merge grids (padded to whole XCD rounds) must fit their limit
+  const int64_t per_seq = max_partitions(max_seq_len) > 32 ? max_partitions(max_seq_len) : 32;
+  if ((int64_t)num_seqs * cache->num_kv_heads * per_seq + kXcds > 0x7fffffff)
     return PKV_ERR_INVALID_ARGUMENT;
   const size_t need = pkv_paged_attention_workspace_bytes(num_seqs, num_q_tokens, max_seq_len,
                                                           num_q_heads, cache->head_dim);
@@ -448,23 +565,24 @@ static int attention_impl(const pkv_cache_t* cache, int32_t layer, void* out, co
   a.max_q_len = max_q_len;
   a.max_parts = (int)max_partitions(max_seq_len);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int64_t rows = (int64_t)num_seqs * a.max_parts * num_q_heads;
+  const int64_t rows = split_rows(num_seqs, a.max_parts, num_q_heads);
   a.ws_ml = (float*)workspace;
   a.ws_o = (float*)((char*)workspace + round256(rows * 2 * 4));
   a.ws_pf = (char*)workspace + round256(rows * 2 * 4) + round256(rows * (int64_t)cache->head_dim * 4);
   a.pf_items = prefill_items_bound(num_seqs, num_q_tokens, num_q_heads);
   a.ws_plan = (char*)a.ws_pf + round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads));
   a.stream = (hipStream_t)stream;
-  // decode rows (q_len = 1), then prefill chunks: small ones per wavefront, large ones tiled
+  // decode rows and short chunks (q_len * G <= small_cols) in the partitioned kernel,
+  // then longer chunks: tiled (fp32: one wavefront per 16 columns)
   switch (cache->dtype) {
     case PKV_F32: rc = dispatch_d<TF32>(a, cache->head_dim, G); break;
     case PKV_F16: rc = dispatch_d<TF16>(a, cache->head_dim, G); break;
     case PKV_BF16: rc = dispatch_d<TBF16>(a, cache->head_dim, G); break;
     default: return PKV_ERR_UNSUPPORTED;
   }
-  if (rc != PKV_OK || max_q_len <= 1) return rc;
-  rc = launch_prefill_small(a, cache->dtype, cache->head_dim, G);
-  if (rc != PKV_OK || (int64_t)max_q_len * G <= kSmallChunkCols) return rc;
+  const int small_cols = small_chunk_max_cols(cache->dtype, cache->head_dim);
+  if (rc != PKV_OK || (int64_t)max_q_len * G <= small_cols) return rc;
+  if (cache->dtype == PKV_F32) return launch_prefill_wave(a, cache->dtype, cache->head_dim, G);
   return launch_prefill_tiled(a, cache->dtype, cache->head_dim, G);
 }
 

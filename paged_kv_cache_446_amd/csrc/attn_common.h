@@ -13,6 +13,20 @@
 namespace pkv {
 
 constexpr int kWaves = 4;  // wavefronts per decode workgroup
+constexpr int kXcds = 8;   // accelerator complex dies of an MI355X
+
+// Workgroup id -> index into a list of `live` work units.  Dispatch deals
+// consecutive ids round-robin over the XCDs; unit j = (id % 8) * C + id / 8
+// with C = ceil(live / 8) gives every XCD one contiguous run of units.  Ids
+// whose unit is past the list (the grid is sized for the worst case) come
+// last in dispatch order and return at once; returns -1 for them.
+__device__ __forceinline__ int xcd_unit(int id, int live) {
+  const int per = (live + kXcds - 1) / kXcds;
+  const int r = id / kXcds;
+  if (r >= per) return -1;
+  const int j = (id % kXcds) * per + r;
+  return j < live ? j : -1;
+}
 
 typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
 
@@ -177,6 +191,24 @@ __device__ __forceinline__ void store_elem(typename DT::T* out, int64_t i, float
     out[i] = (typename DT::T)v;
 }
 
+// Four consecutive outputs (i a multiple of 4), rounded to the output type.
+template <class DT>
+__device__ __forceinline__ void store4(typename DT::T* out, int64_t i, f32x4 v) {
+  if constexpr (DT::kBytes == 4) {
+    *(f32x4*)(out + i) = v;
+  } else {
+    uint2 pk;
+    if constexpr (__is_same(DT, TBF16)) {
+      pk.x = pack2_bf16(v[0], v[1]);
+      pk.y = pack2_bf16(v[2], v[3]);
+    } else {
+      pk.x = pack2_f16(v[0], v[1]);
+      pk.y = pack2_f16(v[2], v[3]);
+    }
+    *(uint2*)(out + i) = pk;
+  }
+}
+
 // Arguments of one paged_attention call, as the kernels' launchers see them.
 struct AttnArgs {
   const void* q;
@@ -198,17 +230,22 @@ struct AttnArgs {
   hipStream_t stream;
 };
 
-// Launchers of the prefill kernels (prefill.hip).  Each returns PKV_OK or a
-// PKV_ERR_* status; both only enqueue work on a.stream.
-//   small chunks (q_len * G <= 64 columns): one wavefront per 16 columns
-//   large chunks: planned work list + LDS-tiled persistent kernel
-int launch_prefill_small(const AttnArgs& a, int dtype, int head_dim, int G);
+// Launchers of the prefill kernels (prefill.hip) for chunks wider than
+// small_chunk_max_cols (query token, head) columns; narrower rows take the
+// partitioned decode kernel.  Each returns PKV_OK or a PKV_ERR_* status and
+// only enqueues work on a.stream.
+//   16-bit types: planned work list + LDS-tiled persistent kernel
+//   fp32: one wavefront per 16 columns
+int launch_prefill_wave(const AttnArgs& a, int dtype, int head_dim, int G);
 int launch_prefill_tiled(const AttnArgs& a, int dtype, int head_dim, int G);
+// Widest row, in (query token, head) columns, the decode kernel takes: two
+// 16-column tiles per wavefront for 16-bit types up to head_dim 128, else one.
+inline int small_chunk_max_cols(int dtype, int head_dim) {
+  return (dtype != PKV_F32 && head_dim <= 128) ? 32 : 16;
+}
 // Bound on the tiled prefill's work items, and the workspace bytes they and the
 // queue counters take.
 int64_t prefill_items_bound(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads);
 int64_t prefill_workspace_bytes(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads);
-// Columns (query token, head pairs) at or below which a chunk takes the small kernel.
-constexpr int kSmallChunkCols = 64;
 
 }  // namespace pkv

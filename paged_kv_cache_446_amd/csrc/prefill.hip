@@ -6,9 +6,9 @@
 // "PagedAttention").
 //
 // Two kernels:
-//   * small chunks (q_len * G <= 64 (query token, head) columns, e.g. the
-//     verify step of speculative decoding): one wavefront per 16 columns,
-//     K/V tiles straight from memory into registers;
+//   * small chunks (q_len * G <= 32 (query token, head) columns, e.g. the
+//     verify step of speculative decoding): decode-style, one workgroup per
+//     (sequence, KV head) whose wavefronts split the context's blocks;
 //   * large chunks: a plan kernel lists (sequence, 256-column query tile, KV
 //     head) items, longest context first, and a persistent kernel takes them
 //     from a queue.  Per item, K/V tiles of two blocks at a time are staged
@@ -20,17 +20,18 @@
 namespace pkv {
 
 // ---------------------------------------------------------------------------
-// Small chunks: grid (num_kv_heads * q_tiles, num_seqs), 4 wavefronts.  Each
+// fp32 chunks wider than the small kernel's columns (there is no fp32 tiled
+// kernel): grid (num_kv_heads * q_tiles, num_seqs), 4 wavefronts.  Each
 // wavefront owns 16/G query tokens x G heads (one 16-column tile) and scans
-// every block its last token can see, causal inside the chunk.  Chunks with
-// more than max_cols columns are left to the tiled kernel.
+// every block its last token can see, causal inside the chunk.  Chunks of at
+// most min_cols columns are left to the small kernel.
 // ---------------------------------------------------------------------------
 template <class DT, int D, int G>
-__global__ __launch_bounds__(256) void prefill_small_kernel(
+__global__ __launch_bounds__(256) void prefill_wave_kernel(
     const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
     const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
     const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ qsl, int num_kv_heads, float scale_log2, int max_cols) {
+    const int32_t* __restrict__ qsl, int num_kv_heads, float scale_log2, int min_cols) {
   typedef Geo<DT, D> Gm;
   constexpr int kTokW = 16 / G;            // query tokens per wavefront
   constexpr int kTokWG = kWaves * kTokW;   // query tokens per workgroup
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void prefill_small_kernel(
   const int tile = blockIdx.x / num_kv_heads;
   const int qb = qsl[s];
   const int q_len = qsl[s + 1] - qb;
-  if (q_len <= 1 || (int64_t)q_len * G > max_cols) return;
+  if (q_len <= 1 || (int64_t)q_len * G <= min_cols) return;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
@@ -136,8 +137,8 @@ struct PfItem {
 // resets the queue: queue[0] = next item, queue[1] = number of items.
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int num_seqs,
-    int num_kv_heads, int G, int cols, PfItem* __restrict__ items, int32_t* __restrict__ queue,
-    int max_items) {
+    int num_kv_heads, int G, int cols, int small_cols, PfItem* __restrict__ items,
+    int32_t* __restrict__ queue, int max_items) {
   __shared__ int hist[kPfBuckets], base[kPfBuckets];
   const int tid = threadIdx.x;
   const int qt_tokens = cols / G;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
   for (int pass = 0; pass < 2; ++pass) {
     for (int s = tid; s < num_seqs; s += blockDim.x) {
       const int qb = qsl[s], q_len = qsl[s + 1] - qb, n = seq_lens[s];
-      if ((int64_t)q_len * G <= kSmallChunkCols) continue;
+      if ((int64_t)q_len * G <= small_cols) continue;
       const int ctx = n - q_len;
       const int nqt = (q_len + qt_tokens - 1) / qt_tokens;
       for (int t = 0; t < nqt; ++t) {
@@ -174,22 +175,6 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
 }
 
 // four consecutive output elements of one row (fp32 -> storage type, RNE)
-template <class DT>
-__device__ __forceinline__ void store4(typename DT::T* out, int64_t i, f32x4 v) {
-  if constexpr (DT::kBytes == 4) {
-    *(f32x4*)(out + i) = v;
-  } else {
-    uint2 pk;
-    if constexpr (__is_same(DT, TBF16)) {
-      pk.x = pack2_bf16(v[0], v[1]);
-      pk.y = pack2_bf16(v[2], v[3]);
-    } else {
-      pk.x = pack2_f16(v[0], v[1]);
-      pk.y = pack2_f16(v[2], v[3]);
-    }
-    *(uint2*)(out + i) = pk;
-  }
-}
 
 // max over the four lanes c, c+16, c+32, c+48 of a column (row swaps, no LDS)
 __device__ __forceinline__ float col_max4(float x) {
@@ -446,14 +431,13 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
 // host side
 // ---------------------------------------------------------------------------
 template <class DT, int D, int G>
-static int small_launch(const AttnArgs& a, int max_cols) {
+static int wave_launch(const AttnArgs& a) {
   typedef typename DT::T T;
   constexpr int kTokWG = kWaves * (16 / G);
-  const int64_t max_tok = min((int64_t)a.max_q_len, (int64_t)max_cols / G);
-  dim3 grid(a.num_kv_heads * (unsigned)((max_tok + kTokWG - 1) / kTokWG), a.num_seqs);
-  hipLaunchKernelGGL((prefill_small_kernel<DT, D, G>), grid, dim3(256), 0, a.stream,
-                     (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
-                     a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, max_cols);
+  dim3 grid(a.num_kv_heads * (unsigned)((a.max_q_len + kTokWG - 1) / kTokWG), a.num_seqs);
+  hipLaunchKernelGGL((prefill_wave_kernel<DT, D, G>), grid, dim3(256), 0, a.stream, (const T*)a.q,
+                     (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride, a.seq_lens,
+                     a.qsl, a.num_kv_heads, a.scale_log2, 16);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -474,7 +458,9 @@ static int tiled_launch(const AttnArgs& a) {
   PfItem* items = (PfItem*)a.ws_pf;
   int32_t* queue = (int32_t*)((char*)a.ws_pf + a.pf_items * sizeof(PfItem));
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
-                     a.num_seqs, a.num_kv_heads, G, P::kCols, items, queue, (int)a.pf_items);
+                     a.num_seqs, a.num_kv_heads, G, P::kCols,
+                     small_chunk_max_cols(DT::kBytes == 2 ? PKV_BF16 : PKV_F32, D), items, queue,
+                     (int)a.pf_items);
   hipLaunchKernelGGL((prefill_tiled_kernel<DT, D, G>), dim3(grid), dim3(kPfThreads), P::kLdsBytes,
                      a.stream, (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt,
                      a.bt_stride, a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, items, queue);
@@ -482,24 +468,12 @@ static int tiled_launch(const AttnArgs& a) {
 }
 
 template <class DT, int D>
-static int small_g(const AttnArgs& a, int G, int max_cols) {
+static int wave_g(const AttnArgs& a, int G) {
   switch (G) {
-    case 1: return small_launch<DT, D, 1>(a, max_cols);
-    case 2: return small_launch<DT, D, 2>(a, max_cols);
-    case 4: return small_launch<DT, D, 4>(a, max_cols);
-    case 8: return small_launch<DT, D, 8>(a, max_cols);
-  }
-  return PKV_ERR_UNSUPPORTED;
-}
-
-template <class DT>
-static int small_d(const AttnArgs& a, int D, int G, int max_cols) {
-  switch (D) {
-    case 64: return small_g<DT, 64>(a, G, max_cols);
-    case 128: return small_g<DT, 128>(a, G, max_cols);
-    case 256:
-      if constexpr (DT::kBytes == 2) return small_g<DT, 256>(a, G, max_cols);
-      break;
+    case 1: return wave_launch<DT, D, 1>(a);
+    case 2: return wave_launch<DT, D, 2>(a);
+    case 4: return wave_launch<DT, D, 4>(a);
+    case 8: return wave_launch<DT, D, 8>(a);
   }
   return PKV_ERR_UNSUPPORTED;
 }
@@ -525,12 +499,11 @@ static int tiled_d(const AttnArgs& a, int D, int G) {
   return PKV_ERR_UNSUPPORTED;
 }
 
-int launch_prefill_small(const AttnArgs& a, int dtype, int head_dim, int G) {
-  // fp32 has no tiled kernel: every chunk takes the per-wavefront kernel
-  switch (dtype) {
-    case PKV_F32: return small_d<TF32>(a, head_dim, G, 0x7fffffff);
-    case PKV_F16: return small_d<TF16>(a, head_dim, G, kSmallChunkCols);
-    case PKV_BF16: return small_d<TBF16>(a, head_dim, G, kSmallChunkCols);
+int launch_prefill_wave(const AttnArgs& a, int dtype, int head_dim, int G) {
+  if (dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  switch (head_dim) {
+    case 64: return wave_g<TF32, 64>(a, G);
+    case 128: return wave_g<TF32, 128>(a, G);
   }
   return PKV_ERR_UNSUPPORTED;
 }

@@ -139,9 +139,10 @@ def test_shared_prefix_equals_private_copies_bitwise():
     assert len(rs.flow.step.pairs) == 3  # even sequences copied the last shared block
 
 
-# Large chunks take the LDS-tiled prefill kernel (more than 64 (token, head)
-# columns): several query tiles per chunk, contexts of zero, one block, odd
-# block counts and past a partition, next to decode rows and small chunks.
+# Large chunks take the LDS-tiled prefill kernel (16-bit chunks of more than 32
+# (token, head) columns, 16 at head_dim 256): several query tiles per chunk,
+# contexts of zero, one block, odd block counts and past a partition, next to
+# decode rows and small chunks.
 @pytest.mark.parametrize("dtype,hq,hkv,d", [
     ("bf16", 32, 8, 128), ("f16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 16, 8, 64),
     ("f16", 16, 2, 256), ("bf16", 64, 8, 128), ("bf16", 8, 4, 64),
@@ -168,6 +169,78 @@ def test_prefill_tiled_deterministic_and_placement_invariant():
     other = np.random.default_rng(78).permutation(spec.num_blocks).astype(np.int32)
     b = gp.prepare(spec, free_order=other)
     assert np.array_equal(first, b.out_bits())
+
+
+# Speculative-decoding verification: every sequence appends k+1 = 2..9 tokens
+# (blog page, advanced features) and they attend causally to the paged context
+# and to each other.  Chunks of up to 32 (token, head) columns take the small
+# kernel whose wavefronts split the context's blocks; wider ones the tiled
+# kernel (fp32: the per-wavefront kernel).
+@pytest.mark.parametrize("dtype,hq,hkv,d", [
+    ("bf16", 32, 8, 128), ("f16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 16, 8, 64),
+    ("bf16", 64, 8, 128), ("f16", 16, 2, 256), ("bf16", 8, 4, 256), ("f32", 32, 8, 128),
+    ("f32", 8, 8, 64),
+])
+def test_verify_chunks(dtype, hq, hkv, d):
+    q = np.arange(16) % 8 + 2  # k+1 = 2..9, twice
+    spec = workloads.verify_spec(num_seqs=16, max_len=2600, q_len=q, variant=1, dtype=dtype,
+                                 hq=hq, hkv=hkv, d=d)
+    _check(spec, f"verify {dtype} {hq}/{hkv} d{d}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_verify_column_boundaries(G):
+    # q_len * G on either side of 16 and 32 columns (one and two column tiles),
+    # over contexts of zero, a partial block, exact blocks and several thousand tokens
+    cols = [16, 17, 32, 33, 8, 24]
+    q = np.array([max(2, -(-c // G)) for c in cols] * 2, dtype=np.int64)
+    ctx = np.array([0, 5, 16, 64, 1000, 3001, 47, 2048, 1, 15, 4095, 300], dtype=np.int64)
+    spec = workloads.make_spec(f"vb-{G}", (446, 99, G), "bf16", 8 * G, 8, 128, ctx, q)
+    _check(spec, f"verify boundaries G={G}")
+
+
+@pytest.mark.parametrize("q_len,G", [(2, 4), (5, 4), (9, 2), (8, 4), (3, 8)])
+def test_verify_partition_starts_inside_the_chunk(q_len, G):
+    # the last 1024-token partition of the context begins among the chunk's own
+    # tokens, so the chunk's first tokens see nothing of it
+    ctx = np.array([1024 - j for j in range(1, q_len)] + [2048 - 1, 3072 - q_len + 1, 4096 - 1],
+                   dtype=np.int64)
+    q = np.full(len(ctx), q_len, dtype=np.int64)
+    spec = workloads.make_spec(f"vp-{q_len}-{G}", (446, 100, q_len, G), "bf16", 8 * G, 8, 128, ctx, q)
+    _check(spec, f"verify partition inside chunk q={q_len} G={G}")
+
+
+def test_verify_long_rows_take_larger_partitions():
+    # every row at the longest context: the split rows would not fit the workspace
+    # with 1024-token partitions, so the plan doubles them (twice here); a decode
+    # row in the same batch keeps 1024-token partitions
+    n = np.array([8192, 8192, 8192, 8191, 8192], dtype=np.int64)
+    q = np.array([8, 8, 7, 8, 1], dtype=np.int64)
+    spec = workloads.make_spec("vlong", (446, 101), "bf16", 32, 8, 128, n - q, q)
+    _check(spec, "verify long rows")
+
+
+def test_verify_full_size_sampled():
+    # the verify workload at full size (256 sequences, contexts up to 8192,
+    # k+1 = 5): a spread of sequences against the oracle, every row finite
+    import torch
+
+    gp = _gp()
+    spec = workloads.verify_spec()
+    run = gp.prepare(spec)
+    got = numerics.to_f64(run.out_bits(), spec.dtype).reshape(spec.num_q_tokens, spec.num_q_heads,
+                                                               spec.head_dim)
+    order = np.argsort(spec.seq_lens, kind="stable")
+    seqs = sorted(set(int(i) for i in order[np.linspace(0, spec.num_seqs - 1, 8).astype(int)]))
+    ref = op.run(spec, seqs=seqs)
+    rows = np.concatenate([np.arange(spec.query_start_loc[s], spec.query_start_loc[s + 1]) for s in seqs])
+    ok, worst = gp.compare(got[rows], ref.out[rows], spec.dtype)
+    gp.log(f"[attn] verify full size: {len(seqs)} sequences, worst {worst:.3g}")
+    assert ok and np.isfinite(got).all()
+    bits = run.out_bits().copy()
+    gp.attention(run)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits, run.out_bits())
 
 
 def _contiguous_pool(spec, gp):
@@ -234,6 +307,42 @@ def test_contiguous_baseline_equals_paged_bitwise(dtype, hq, hkv, d):
                                 spec.query_start_loc, spec.scale, dtype)
     ok, worst = gp.compare(numerics.to_f64(bc, dtype).reshape(ref.shape), ref, dtype)
     assert ok, worst
+
+
+def test_contiguous_baseline_leaves_chunk_rows_unwritten():
+    # the table-free baseline takes decode rows only: rows of short chunks keep
+    # whatever the output held, decode rows equal the paged kernel's bitwise
+    import torch
+
+    from paged_kv_cache_446_amd import ops
+
+    gp = _gp()
+    ctx = np.array([1500, 40, 2100, 7, 999], dtype=np.int64)
+    q_lens = np.array([1, 3, 1, 2, 1], dtype=np.int64)
+    spec = workloads.make_spec("contig-mixed", (446, 102), "bf16", 8, 2, 64, ctx, q_lens)
+    cache, kp_h, vp_h, tables, first = _contiguous_pool(spec, gp)
+    q = gp.dev_bits(spec.all_q_bits(), "bf16")
+    sl = torch.from_numpy(spec.seq_lens.astype(np.int32)).to("cuda:0")
+    qsl = torch.from_numpy(spec.query_start_loc).to("cuda:0")
+    maxn = int(spec.seq_lens.max())
+    ws = torch.empty(ops.workspace_bytes(spec.num_seqs, spec.num_q_tokens, maxn, 8, 64),
+                     dtype=torch.uint8, device="cuda:0")
+    out_p = torch.zeros_like(q)
+    out_c = torch.full_like(q, 7)
+    ops.paged_attention(cache, out_p, q, torch.from_numpy(tables).to("cuda:0"), sl, qsl,
+                        num_q_heads=8, max_q_len=3, max_seq_len=maxn, scale=spec.scale, workspace=ws)
+    ops.contiguous_attention(cache, out_c, q, torch.from_numpy(first).to("cuda:0"), sl, qsl,
+                             num_q_heads=8, max_seq_len=maxn, scale=spec.scale, workspace=ws)
+    torch.cuda.synchronize()
+    bp = gp.host_bits(out_p, "bf16").reshape(spec.num_q_tokens, -1)
+    bc = gp.host_bits(out_c, "bf16").reshape(spec.num_q_tokens, -1)
+    qsl_h = spec.query_start_loc
+    for s_ in range(spec.num_seqs):
+        rows = slice(int(qsl_h[s_]), int(qsl_h[s_ + 1]))
+        if q_lens[s_] == 1:
+            assert np.array_equal(bp[rows], bc[rows])
+        else:
+            assert (bc[rows] == 7).all()
 
 
 @pytest.mark.parametrize("prefix,tail_a,tail_b,q_b", [(1000, 37, 50, 1), (10000, 5, 256, 256), (40, 0, 9, 9)])

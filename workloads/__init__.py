@@ -12,6 +12,7 @@ from .generate import (  # noqa: F401
     make_spec,
     named_spec,
     scaled_spec,
+    verify_spec,
     CONFIG_NAMES,
     run_flow,
     Flow,

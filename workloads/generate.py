@@ -178,8 +178,27 @@ def _log_uniform(rng, lo, hi, size) -> np.ndarray:
 
 
 def named_spec(name: str) -> Spec:
-    """The five full-size configurations."""
+    """The five full-size configurations, or the verify workload."""
+    if name == "verify":
+        return verify_spec()
     return scaled_spec(name)
+
+
+def verify_spec(num_seqs: Optional[int] = None, max_len: Optional[int] = None, q_len: int = 5,
+                variant: int = 0, dtype: str = "bf16", hq: int = 32, hkv: int = 8,
+                d: int = 128) -> Spec:
+    """Speculative-decoding verification (blog page, advanced features): every
+    sequence appends ``q_len`` = k+1 tokens (the last accepted token and k
+    drafted ones) in one pass, over the Llama-3-8B-shaped GQA decode batch's
+    contexts (log-uniform in [64, 8192]).  ``q_len`` may be a scalar or one
+    length per sequence."""
+    key = (446, 6) if variant == 0 else (446, 6, 7, variant)
+    rng = np.random.default_rng(list(key))
+    S = num_seqs or 256
+    hi = min(8192, max_len or 8192)
+    n = _log_uniform(rng, min(64, hi), hi, S)
+    q = np.broadcast_to(np.asarray(q_len, dtype=np.int64), (S,)).copy()
+    return make_spec("verify", key, dtype, hq, hkv, d, n - 1, q, rng=rng)
 
 
 def scaled_spec(name: str, num_seqs: Optional[int] = None, max_len: Optional[int] = None,
