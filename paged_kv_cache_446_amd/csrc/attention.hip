@@ -56,12 +56,24 @@ constexpr int decode_occupancy() {
   return (DT::kBytes == 2 && D <= 128) ? (CT == 1 ? 3 : 2) : 1;
 }
 
-// Work lists of one call, written by decode_plan_kernel.  An item is
-// (sequence, partition, first block, end block); the lists hold the items of
-// one-tile rows, then (from offset cap) those of two-tile rows, each in
-// sequence order.  Sequences split over several partitions are listed in merge
-// and own workspace rows from base[s]: row base[s] + (p * q_len + t) * Hq + head
-// holds partition p's result for query token t.
+// Work of one decode workgroup, as decode_plan_kernel writes it: sequence s,
+// KV head h, blocks [b0, b1) (partition part of the row), the row's first query
+// row qb, its query tokens and sequence length, and the workspace row of
+// (this partition, token 0, head h*G) if the row is split over partitions
+// (wrow < 0 otherwise).  One 48-byte record, read with two scalar loads.
+struct alignas(16) DecodeItem {
+  int32_t s, h, b0, b1, qb, q_len, n, part;
+  int64_t wrow, unused;
+};
+
+// Work lists of one call, written by decode_plan_kernel: the items of one-tile
+// rows (class 1) and of two-tile rows (class 2), each in sequence order, with
+// h = 0.  Workgroup units are (item, KV head) pairs, item-major, dealt to the
+// eight XCDs in contiguous runs (xcd_unit), so the KV heads of a partition and
+// neighbouring partitions share an XCD.  Sequences split over several
+// partitions own workspace rows from base[s]: row base[s] + (p * q_len + t) * Hq
+// + head holds partition p's result for query token t; one merge entry per
+// (split sequence, query token).
 // One merge: the output query row, the partition count, the workspace row of
 // (partition 0, this token, head 0) and the rows between partitions.
 struct MergeEntry {
@@ -70,9 +82,9 @@ struct MergeEntry {
 };
 
 struct DecodePlan {
-  int32_t* counts;    // [0] one-tile items, [1] merges, [2] two-tile items;
+  int32_t* counts;    // [0] class-1 items, [1] merges, [2] class-2 items;
                       // nullptr: no plan, every row is one item (single-partition batches)
-  int4* items;        // [2 * cap]
+  DecodeItem* items;  // [2][cap]
   MergeEntry* merge;  // [num_seqs * 32]
   int64_t* base;      // [num_seqs]
   int num_seqs;
@@ -181,13 +193,16 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
     if (!cls) continue;
     const int n = seq_lens[s], nb = blocks(n), pb = part_blocks(q_len, shift);
     const int np = n > 0 ? (nb + pb - 1) / pb : 1;
-    int4* dst = plan.items + (cls == 1 ? (int64_t)p1 : (int64_t)plan.cap + p2);
-    for (int p = 0; p < np; ++p) dst[p] = int4{s, p, p * pb, min(nb, (p + 1) * pb)};
+    const int qb = qsl[s];
+    DecodeItem* rec = plan.items + (cls == 1 ? (int64_t)p1 : (int64_t)plan.cap + p2);
+    for (int p = 0; p < np; ++p)
+      rec[p] = DecodeItem{s, 0, p * pb, min(nb, (p + 1) * pb), qb, q_len, n, p,
+                          np > 1 ? pr + (long long)p * q_len * hq : -1, 0};
     (cls == 1 ? p1 : p2) += np;
     if (np > 1) {
       for (int t = 0; t < q_len; ++t)
         plan.merge[pm++] =
-            MergeEntry{qsl[s] + t, np, 0, 0, pr + (long long)t * hq, (long long)q_len * hq};
+            MergeEntry{qb + t, np, 0, 0, pr + (long long)t * hq, (long long)q_len * hq};
       plan.base[s] = pr;
       pr += (long long)np * q_len * hq;
     }
@@ -209,41 +224,53 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
                    float* __restrict__ ws_o, float* __restrict__ ws_ml, DecodePlan plan,
                    int contiguous) {
   typedef Geo<DT, D> Gm;
-  const int live = (plan.counts ? plan.counts[CT == 1 ? 0 : 2] : plan.num_seqs) * num_kv_heads;
-  const int j = xcd_unit(blockIdx.x, live);
-  if (j < 0) return;
-  const int h = j % num_kv_heads;
-  const int4 item = plan.counts ? plan.items[(CT == 1 ? 0 : (int64_t)plan.cap) + j / num_kv_heads]
-                                : int4{j / num_kv_heads, 0, 0, kPartBlocks};
-  const int s = item.x, part = item.y, b0 = item.z;
+  // The work item's fields are pinned where they are loaded (an empty asm reads
+  // them), so that the metadata loads of a path issue together, in one round trip,
+  // and are not merged into one load after the paths join.
+  DecodeItem it;
+  if (plan.counts) {
+    const int j = xcd_unit(blockIdx.x, plan.counts[CT == 1 ? 0 : 2] * num_kv_heads);
+    if (j < 0) return;
+    it = plan.items[(CT == 1 ? 0 : (int64_t)plan.cap) + j / num_kv_heads];
+    asm volatile("" : "+s"(it.s), "+s"(it.b0), "+s"(it.b1), "+s"(it.qb), "+s"(it.q_len),
+                 "+s"(it.n), "+s"(it.part), "+s"(it.wrow));
+    it.h = j % num_kv_heads;
+    if (it.wrow >= 0) it.wrow += it.h * G;
+  } else {  // one partition per row: every sequence is an item
+    const int j = xcd_unit(blockIdx.x, plan.num_seqs * num_kv_heads);
+    if (j < 0) return;
+    const int s = j / num_kv_heads;
+    int q0 = qsl[s], q1 = qsl[s + 1], n = seq_lens[s];
+    asm volatile("" : "+s"(q0), "+s"(q1), "+s"(n));
+    it = DecodeItem{s, j % num_kv_heads, 0, kPartBlocks, q0, q1 - q0, n, 0, -1, 0};
+    const int cols = it.q_len * G;
+    if (it.q_len < 1 || it.q_len > max_q || cols > CT * 16 || cols <= (CT - 1) * 16) return;
+  }
+  const int s = it.s, h = it.h, b0 = it.b0, qb = it.qb, q_len = it.q_len, n = it.n;
+  const int cols = q_len * G;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int32_t* btr = bt + (int64_t)s * bt_stride;
-  // block-table entries of this wavefront's first blocks b0 + w + 4i, one per lane,
-  // loaded alongside the sequence metadata (bounded by the item and the table width).
-  // Contiguous storage (the baseline without paging): bt[s] is the sequence's
-  // first block and block i is bt[s] + i.
+  // block-table entries of this wavefront's first blocks b0 + w + 4i, one per lane
+  // (bounded by the item and the table width).  Contiguous storage (the baseline
+  // without paging): bt[s] is the sequence's first block and block i is bt[s] + i.
   auto table = [&](int i) {  // entry of this wavefront's block i (relative), or 0
     const int bi = b0 + w + kWaves * i;
-    return (bi < item.w && bi < bt_stride) ? (contiguous ? bt[s] + bi : btr[bi]) : 0;
+    return (bi < it.b1 && bi < bt_stride) ? (contiguous ? bt[s] + bi : btr[bi]) : 0;
   };
   int btv = table(lane);
-  const int qb = qsl[s], q_len = qsl[s + 1] - qb;
-  const int n = seq_lens[s];
-  const int cols = q_len * G;
-  if (q_len < 1 || q_len > max_q || cols > CT * 16 || cols <= (CT - 1) * 16) return;  // not ours
   const int hq = num_kv_heads * G;
   if (n <= 0) {
-    if (part == 0)
+    if (it.part == 0)
       for (int e = threadIdx.x; e < cols * D; e += blockDim.x)
         store_elem<DT>(out, ((int64_t)(qb + e / D / G) * hq + h * G + (e / D) % G) * D + e % D, 0.f);
     return;
   }
   // a sequence longer than the bounds the host passed is cut at them (never read past them)
   const int nblocks = min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks));
-  const int b1 = min(nblocks, item.w);
+  const int b1 = min(nblocks, it.b1);
   if (b0 >= b1) return;
-  const bool split = b0 > 0 || b1 < nblocks;  // the row has other partitions
+  const bool split = it.wrow >= 0;  // the row has other partitions
   const int ctx = n - q_len;
   const int g = lane >> 4, c = lane & 15;
 
@@ -318,7 +345,6 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
     }
   }
   __syncthreads();
-  const int64_t wrow0 = split ? plan.base[s] + (int64_t)part * q_len * hq : 0;
   for (int e = threadIdx.x; e < cols * D; e += blockDim.x) {
     const int col = e / D, d = e - col * D;
     float M = sm_m[0][col];
@@ -335,11 +361,11 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
       den += f * sm_l[ww][col];
     }
     const float o = den > 0.f ? num / den : 0.f;
-    const int64_t qrow = (int64_t)(col / G) * hq + h * G + col % G;  // within the row's tokens
+    const int64_t qrow = (int64_t)(col / G) * hq + col % G;  // from (token 0, head h*G)
     if (!split) {
-      store_elem<DT>(out, ((int64_t)qb * hq + qrow) * D + d, o);
+      store_elem<DT>(out, ((int64_t)qb * hq + h * G + qrow) * D + d, o);
     } else {
-      const int64_t idx = wrow0 + qrow;
+      const int64_t idx = it.wrow + qrow;
       ws_o[idx * D + d] = o;
       if (d == 0) {
         ws_ml[2 * idx] = M;
@@ -408,9 +434,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 
 static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
-// counts, two item lists, merge entries (up to 32 query tokens per sequence), row bases
+// counts, the item records of two classes, merge entries (up to 32 query tokens per
+// sequence), row bases
+static int64_t plan_item_bytes(int64_t num_seqs, int64_t max_parts) {
+  return round256(256 + 2 * num_seqs * max_parts * (int64_t)sizeof(DecodeItem));
+}
 static int64_t decode_plan_bytes(int64_t num_seqs, int64_t max_parts) {
-  return round256(256 + 2 * num_seqs * max_parts * (int64_t)sizeof(int4)) +
+  return plan_item_bytes(num_seqs, max_parts) +
          round256(num_seqs * 32 * (int64_t)sizeof(MergeEntry)) + round256(num_seqs * 8);
 }
 
@@ -447,8 +477,8 @@ static int launch(const AttnArgs& a) {
   if (a.max_parts > 1) {
     // sequences may span several partitions: list the live (sequence, partition) items
     plan.counts = (int32_t*)a.ws_plan;
-    plan.items = (int4*)((char*)a.ws_plan + 256);
-    char* mp = (char*)a.ws_plan + round256(256 + 2 * (int64_t)plan.cap * sizeof(int4));
+    plan.items = (DecodeItem*)((char*)a.ws_plan + 256);
+    char* mp = (char*)a.ws_plan + plan_item_bytes(a.num_seqs, a.max_parts);
     plan.merge = (MergeEntry*)mp;
     plan.base = (int64_t*)(mp + round256((int64_t)a.num_seqs * 32 * sizeof(MergeEntry)));
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
