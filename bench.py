@@ -93,7 +93,7 @@ def measured_traffic():
     try:
         txt = open(prof).read()
         h = hashlib.sha256()
-        for f in ("attention.hip", "pkv_device.h"):
+        for f in ("attention.hip", "attn_common.h", "pkv_device.h"):
             h.update(open(os.path.join(csrc, f), "rb").read())
     except OSError:
         return None
