@@ -452,7 +452,7 @@ static int64_t split_rows(int64_t num_seqs, int64_t max_parts, int64_t num_q_hea
 }
 
 template <class DT, int D, int G, int CT>
-static void launch_ct(const AttnArgs& a, const DecodePlan& plan) {
+static int launch_ct(const AttnArgs& a, const DecodePlan& plan) {
   typedef typename DT::T T;
   // grids sized for every sequence in every partition; the plan's counts cut them short
   const int64_t units = (int64_t)a.num_kv_heads * a.max_parts * a.num_seqs;
@@ -461,6 +461,7 @@ static void launch_ct(const AttnArgs& a, const DecodePlan& plan) {
                      (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
                      a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, a.max_parts, a.max_q_len,
                      a.ws_o, a.ws_ml, plan, a.contiguous);
+  return PKV_OK;
 }
 
 template <class DT, int D, int G>
@@ -486,9 +487,12 @@ static int launch(const AttnArgs& a) {
                        a.num_kv_heads * G,
                        (long long)split_rows(a.num_seqs, a.max_parts, a.num_kv_heads * G), plan);
   }
-  launch_ct<DT, D, G, 1>(a, plan);
+  // a class no row can be in is not launched: two-tile rows need max_q_len * G > 16,
+  // and rows of one q_len are all in the same class
+  const int64_t widest = (int64_t)a.max_q_len * G;
+  if (!(a.uniform_q && widest > 16) && launch_ct<DT, D, G, 1>(a, plan) != PKV_OK) return PKV_ERR_HIP;
   if constexpr (kMaxCols > 16)
-    if ((int64_t)a.max_q_len * G > 16) launch_ct<DT, D, G, 2>(a, plan);
+    if (widest > 16 && launch_ct<DT, D, G, 2>(a, plan) != PKV_OK) return PKV_ERR_HIP;
   if (a.max_parts > 1) {
     // merge entries: at most one per query token of the rows this kernel takes
     const int64_t qmax = a.max_q_len < kMaxCols / G ? a.max_q_len : kMaxCols / G;
@@ -542,7 +546,7 @@ extern "C" size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t 
   // split rows' (m, l) pairs and partition outputs, prefill work list, decode plan; each
   // section 256-byte aligned
   return (size_t)(round256(rows * 2 * 4) + round256(rows * (int64_t)head_dim * 4) +
-                  round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads)) +
+                  round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, head_dim)) +
                   decode_plan_bytes(num_seqs, parts));
 }
 
@@ -594,23 +598,28 @@ static int attention_impl(const pkv_cache_t* cache, int32_t layer, void* out, co
   a.num_kv_heads = cache->num_kv_heads;
   a.max_q_len = max_q_len;
   a.max_parts = (int)max_partitions(max_seq_len);
+  a.uniform_q = (int64_t)num_seqs * max_q_len == num_q_tokens;
   a.scale_log2 = scale * 1.4426950408889634f;
   const int64_t rows = split_rows(num_seqs, a.max_parts, num_q_heads);
   a.ws_ml = (float*)workspace;
   a.ws_o = (float*)((char*)workspace + round256(rows * 2 * 4));
   a.ws_pf = (char*)workspace + round256(rows * 2 * 4) + round256(rows * (int64_t)cache->head_dim * 4);
   a.pf_items = prefill_items_bound(num_seqs, num_q_tokens, num_q_heads);
-  a.ws_plan = (char*)a.ws_pf + round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads));
+  a.pf_slots = prefill_slots_bound(num_seqs, num_q_tokens);
+  a.ws_plan = (char*)a.ws_pf + round256(prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads,
+                                                                cache->head_dim));
   a.stream = (hipStream_t)stream;
   // decode rows and short chunks (q_len * G <= small_cols) in the partitioned kernel,
   // then longer chunks: tiled (fp32: one wavefront per 16 columns)
-  switch (cache->dtype) {
-    case PKV_F32: rc = dispatch_d<TF32>(a, cache->head_dim, G); break;
-    case PKV_F16: rc = dispatch_d<TF16>(a, cache->head_dim, G); break;
-    case PKV_BF16: rc = dispatch_d<TBF16>(a, cache->head_dim, G); break;
-    default: return PKV_ERR_UNSUPPORTED;
-  }
   const int small_cols = small_chunk_max_cols(cache->dtype, cache->head_dim);
+  if (!(a.uniform_q && (int64_t)max_q_len * G > small_cols)) {  // some row may be short
+    switch (cache->dtype) {
+      case PKV_F32: rc = dispatch_d<TF32>(a, cache->head_dim, G); break;
+      case PKV_F16: rc = dispatch_d<TF16>(a, cache->head_dim, G); break;
+      case PKV_BF16: rc = dispatch_d<TBF16>(a, cache->head_dim, G); break;
+      default: return PKV_ERR_UNSUPPORTED;
+    }
+  }
   if (rc != PKV_OK || (int64_t)max_q_len * G <= small_cols) return rc;
   if (cache->dtype == PKV_F32) return launch_prefill_wave(a, cache->dtype, cache->head_dim, G);
   return launch_prefill_tiled(a, cache->dtype, cache->head_dim, G);

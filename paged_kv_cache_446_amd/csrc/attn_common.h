@@ -221,11 +221,13 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* qsl;
   int num_seqs, num_kv_heads, max_q_len, max_parts;
+  bool uniform_q;     // every row has max_q_len query tokens (num_q_tokens = num_seqs * max_q_len)
   float scale_log2;
   float* ws_o;
   float* ws_ml;
-  void* ws_pf;        // tiled-prefill work list (pf_items entries) and its queue counters
-  int64_t pf_items;
+  void* ws_pf;        // tiled-prefill work lists, queue counters and split partials
+  int64_t pf_items;   // items bound (q-tile items; each extra piece takes one more slot)
+  int64_t pf_slots;   // partial slots for split items (0: no chunk can exist)
   void* ws_plan;      // decode work lists (decode_plan_kernel)
   hipStream_t stream;
 };
@@ -243,9 +245,11 @@ int launch_prefill_tiled(const AttnArgs& a, int dtype, int head_dim, int G);
 inline int small_chunk_max_cols(int dtype, int head_dim) {
   return (dtype != PKV_F32 && head_dim <= 128) ? 32 : 16;
 }
-// Bound on the tiled prefill's work items, and the workspace bytes they and the
-// queue counters take.
+// Bounds of the tiled prefill's work items and split partial slots, and the
+// workspace bytes they, the merge list and the queue counters take.
 int64_t prefill_items_bound(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads);
-int64_t prefill_workspace_bytes(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads);
+int64_t prefill_slots_bound(int64_t num_seqs, int64_t num_q_tokens);
+int64_t prefill_workspace_bytes(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads,
+                                int64_t head_dim);
 
 }  // namespace pkv

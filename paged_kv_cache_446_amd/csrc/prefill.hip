@@ -3,18 +3,20 @@
 // (blog.mckayzhao.com/?p=56, chunked prefill under advanced features; the
 // mixed {request_id: num_tokens} batch of the V1 section).  Keys are read block
 // by block through the block table, as for decode (same page, section
-// "PagedAttention").
+// "PagedAttention").  Chunks of at most 32 (token, head) columns per KV head
+// take the partitioned decode kernel (attention.hip); this file holds the rest.
 //
-// Two kernels:
-//   * small chunks (q_len * G <= 32 (query token, head) columns, e.g. the
-//     verify step of speculative decoding): decode-style, one workgroup per
-//     (sequence, KV head) whose wavefronts split the context's blocks;
-//   * large chunks: a plan kernel lists (sequence, 256-column query tile, KV
-//     head) items, longest context first, and a persistent kernel takes them
-//     from a queue.  Per item, K/V tiles of two blocks at a time are staged
-//     in LDS (double buffered) and shared by 8 wavefronts of 32 columns; the
-//     scores S^T = K.Q^T use 16x16x32 matrix instructions and the product
-//     O^T += V^T.P^T runs over 32 tokens at a time, also 16x16x32.
+//   * 16-bit types: a plan kernel lists (sequence, 256-column query tile, KV
+//     head, block range) items, longest first, and a persistent kernel takes
+//     them from a queue.  Per item, K/V tiles of several blocks at a time are
+//     staged in LDS (double buffered) and shared by 8 wavefronts of 32
+//     columns; the scores S^T = K.Q^T use 16x16x32 matrix instructions and the
+//     product O^T += V^T.P^T runs over 32 tokens at a time, also 16x16x32.
+//     When a few long items would leave most of the chip idle, the plan cuts
+//     their context into pieces of about one workgroup's share of the work;
+//     pieces write fp32 partials (max, sum, normalised output) and a merge
+//     kernel combines them with the log-sum-exp rule, as decode does.
+//   * fp32: one wavefront per 16 columns.
 #include "attn_common.h"
 
 namespace pkv {
@@ -127,36 +129,150 @@ struct PfGeo {
   static_assert(kLdsBytes + kPfTableMax * 4 + 64 <= 160 * 1024, "LDS of one workgroup");
 };
 
+// A piece of a (sequence, query tile, KV head): blocks [kb0, kb1) of the visible
+// context.  slot < 0: the piece is the whole context and writes the output;
+// otherwise it writes partials to slot (kPfSlotCols columns of (m, l, o)).
 struct PfItem {
-  int32_t s, qtile, h, pad;
+  int32_t s, qtile, h, kb0, kb1, slot, pad0, pad1;
+};
+// One split (sequence, query tile, KV head): its np pieces hold slots slot0 ..
+// slot0 + np - 1, piece p covering the context blocks after those of piece p-1.
+struct PfMerge {
+  int32_t s, qb, q_len, qtile, h, np, slot0, pad;
 };
 
-// Work list of the tiled kernel: one workgroup of 1024 threads.  Items of one
-// (sequence, q-tile) are adjacent (all KV heads); q-tiles are ordered by the
-// context their last row sees, longest first, in 1024-token classes.  Also
-// resets the queue: queue[0] = next item, queue[1] = number of items.
+constexpr int kPfSlotCols = 256;      // columns of a partial slot (the widest item)
+constexpr int kPfSplitWorkers = 256;  // workers the split rule balances over (at most)
+constexpr int kPfMaxSlots = kPfSplitWorkers;  // partial slots of one call
+constexpr int kPfMinPiece = 64;       // blocks of the shortest piece (1024 tokens)
+
+// Byte offsets of the tiled prefill's workspace: items (the q-tile items plus one
+// per extra piece), the plan's (sequence, q-tile) list, merges, queue counters,
+// partial outputs and (m, l) pairs.
+struct PfLayout {
+  int64_t items, tiles, merges, queue, part_o, part_ml, total;
+  PfLayout(int64_t n_items, int64_t slots, int64_t head_dim) {
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    items = 0;
+    tiles = up((n_items + slots) * (int64_t)sizeof(PfItem));  // (sequence, q-tile) list
+    merges = tiles + up(n_items * (int64_t)sizeof(int2));
+    queue = merges + up((slots / 2 + 1) * (int64_t)sizeof(PfMerge));
+    part_o = queue + 256;
+    part_ml = part_o + up(slots * kPfSlotCols * head_dim * 4);
+    total = part_ml + up(slots * kPfSlotCols * 8);
+  }
+};
+
+// Work list of the tiled kernel: one workgroup of 1024 threads.  Every
+// (sequence, q-tile) of a chunk wider than small_cols columns has one item per
+// KV head; items are ordered by the context they read, longest first, in
+// 1024-token classes.  The (sequence, q-tile) pairs are first listed flat
+// (a scan over the sequences), so that the threads share them evenly however
+// they are spread over sequences.
+//
+// Splitting: with W the blocks all items read (over KV heads too) and P the
+// workers, an item of b blocks is cut into np = floor(b P / W) pieces (at least
+// one, each at least kPfMinPiece blocks and a whole number of pipeline steps of
+// sb blocks): items of more than one worker's share are split, and the pieces
+// of all split items number at most P, so one round of workers takes them and
+// max_slots >= P partial slots suffice.  Also resets the queue: queue[0] = next
+// item, queue[1] = number of items, queue[2] = number of merges.
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int num_seqs,
-    int num_kv_heads, int G, int cols, int small_cols, PfItem* __restrict__ items,
-    int32_t* __restrict__ queue, int max_items) {
+    int num_kv_heads, int G, int cols, int small_cols, int bt_stride, int sb, int workers,
+    int max_slots, PfItem* __restrict__ items, int2* __restrict__ tiles,
+    PfMerge* __restrict__ merges, int32_t* __restrict__ queue, int max_items) {
   __shared__ int hist[kPfBuckets], base[kPfBuckets];
-  const int tid = threadIdx.x;
+  __shared__ int sm_tot[1024 / kWave];
+  __shared__ unsigned long long sm_work;
+  __shared__ int sm_slot, sm_merge;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nwaves = blockDim.x / kWave;
   const int qt_tokens = cols / G;
   if (tid < kPfBuckets) hist[tid] = 0;
+  if (tid == 0) {
+    sm_work = 0;
+    sm_slot = 0;
+    sm_merge = 0;
+  }
+  // 1. q-tiles per sequence, an exclusive scan over the sequences (thread t owns
+  //    sequences [t k, t k + k)), and the flat (sequence, q-tile) list
+  const int k = (num_seqs + blockDim.x - 1) / blockDim.x;
+  const int s0 = tid * k;
+  auto ntiles = [&](int s) {
+    const int q_len = qsl[s + 1] - qsl[s];
+    return (int64_t)q_len * G <= small_cols ? 0 : (q_len + qt_tokens - 1) / qt_tokens;
+  };
+  int mine = 0;
+  for (int j = 0; j < k && s0 + j < num_seqs; ++j) mine += ntiles(s0 + j);
+  int x = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) sm_tot[w] = x;
   __syncthreads();
+  int before = 0, total = 0;
+  for (int ww = 0; ww < nwaves; ++ww) {
+    before += ww < w ? sm_tot[ww] : 0;
+    total += sm_tot[ww];
+  }
+  int pos = before + x - mine;
+  for (int j = 0; j < k && s0 + j < num_seqs; ++j) {
+    const int nt = ntiles(s0 + j);
+    for (int t = 0; t < nt; ++t) tiles[pos + t] = int2{s0 + j, t};
+    pos += nt;
+  }
+  __syncthreads();  // the list is visible to the whole workgroup
+  // blocks q-tile t of sequence s reads (the blocks its last row sees)
+  auto vis_blocks = [&](int s, int t) {
+    const int q_len = qsl[s + 1] - qsl[s], n = seq_lens[s];
+    const int vis = n - q_len + min(q_len, (t + 1) * qt_tokens);
+    return (n > 0 && vis > 0) ? min((vis - 1) / kBlock + 1, bt_stride) : 0;
+  };
+  // 2. the work W
+  {
+    unsigned long long wk = 0;
+    for (int i = tid; i < total; i += blockDim.x) {
+      const int2 st = tiles[i];
+      wk += (unsigned long long)vis_blocks(st.x, st.y) * num_kv_heads;
+    }
+    if (wk) atomicAdd(&sm_work, wk);
+  }
+  __syncthreads();
+  const long long W = (long long)sm_work;
+  const bool split = max_slots >= workers && workers > 0 && W > 0;
+  // 3. pieces: counted in pass 0, written in pass 1
   for (int pass = 0; pass < 2; ++pass) {
-    for (int s = tid; s < num_seqs; s += blockDim.x) {
-      const int qb = qsl[s], q_len = qsl[s + 1] - qb, n = seq_lens[s];
-      if ((int64_t)q_len * G <= small_cols) continue;
-      const int ctx = n - q_len;
-      const int nqt = (q_len + qt_tokens - 1) / qt_tokens;
-      for (int t = 0; t < nqt; ++t) {
-        const int vis = max(ctx + min(q_len, (t + 1) * qt_tokens), 0);
-        const int b = kPfBuckets - 1 - min(kPfBuckets - 1, vis >> 10);
-        const int pos = atomicAdd(&hist[b], num_kv_heads);
+    for (int i = tid; i < total; i += blockDim.x) {
+      const int2 st = tiles[i];
+      const int s = st.x, t = st.y;
+      const int vb = vis_blocks(s, t);
+      int np = 1, pl = vb;  // np pieces of pl blocks
+      if (split) {
+        const long long want = min((long long)vb * workers / W, (long long)vb / kPfMinPiece);
+        if (want > 1) {
+          pl = ((vb + (int)want - 1) / (int)want + sb - 1) / sb * sb;
+          np = (vb + pl - 1) / pl;
+        }
+      }
+      int slot0 = -1;
+      if (pass == 1 && np > 1) {
+        slot0 = atomicAdd(&sm_slot, np * num_kv_heads);
+        const int mi = atomicAdd(&sm_merge, num_kv_heads);
+        const int qb = qsl[s], q_len = qsl[s + 1] - qb;
+        for (int h = 0; h < num_kv_heads; ++h)
+          merges[mi + h] = PfMerge{s, qb, q_len, t, h, np, slot0 + h * np, 0};
+      }
+      for (int p = 0; p < np; ++p) {
+        const int kb0 = p * pl, kb1 = min(vb, kb0 + pl);
+        const int b = kPfBuckets - 1 - min(kPfBuckets - 1, ((kb1 - kb0) * kBlock) >> 10);
+        const int at = atomicAdd(&hist[b], num_kv_heads);
         if (pass == 1)
           for (int h = 0; h < num_kv_heads; ++h)
-            if (base[b] + pos + h < max_items) items[base[b] + pos + h] = PfItem{s, t, h, 0};
+            if (base[b] + at + h < max_items)
+              items[base[b] + at + h] =
+                  PfItem{s, t, h, kb0, kb1, np > 1 ? slot0 + h * np + p : -1, 0, 0};
       }
     }
     __syncthreads();
@@ -172,9 +288,8 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
     }
     __syncthreads();
   }
+  if (tid == 0) queue[2] = sm_merge;
 }
-
-// four consecutive output elements of one row (fp32 -> storage type, RNE)
 
 // max over the four lanes c, c+16, c+32, c+48 of a column (row swaps, no LDS)
 __device__ __forceinline__ float col_max4(float x) {
@@ -193,7 +308,8 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
                           const typename DT::T* __restrict__ vp, const int32_t* __restrict__ bt,
                           int bt_stride, const int32_t* __restrict__ seq_lens,
                           const int32_t* __restrict__ qsl, int num_kv_heads, float scale_log2,
-                          const PfItem* __restrict__ items, int32_t* __restrict__ queue) {
+                          const PfItem* __restrict__ items, int32_t* __restrict__ queue,
+                          float* __restrict__ part_o, float2* __restrict__ part_ml) {
   static_assert(DT::kBytes == 2, "16-bit element types");
   typedef Geo<DT, D> Gm;
   typedef PfGeo<DT, D> P;
@@ -221,7 +337,7 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
     __syncthreads();
     if (it >= total) break;
     const PfItem item = items[it];
-    const int s = item.s, h = item.h;
+    const int s = item.s, h = item.h, kb0 = item.kb0, kb1 = item.kb1;
     const int qb = qsl[s], q_len = qsl[s + 1] - qb, n = seq_lens[s];
     const int ctx = n - q_len;
     const int tq0 = item.qtile * QT, tq_end = min(q_len, tq0 + QT);
@@ -252,9 +368,9 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
     const int wave_tq = tq0 + (w * kCT * 16) / G;  // first token of this wavefront
     const bool wave_active = wave_tq < tq_end;
     const int wave_min_lim = ctx + wave_tq;
-    // blocks the tile's last row can see (a sequence with no tokens sees none)
-    const int nvis = n > 0 ? min((ctx + tq_end - 1) / kBlock + 1, bt_stride) : 0;
-    int seg0 = 0;  // first block of the block-table segment held in sm_bt
+    // this item reads blocks [kb0, kb1) of those the tile's last row can see; a piece
+    // boundary other than the last block falls on a whole step
+    int seg0 = kb0;  // first block of the block-table segment held in sm_bt
 
     // K/V of step j: registers -> LDS buffer j & 1; the next kPfDepth-1 steps are in flight.
     // Thread chunk k of a step is chunk ci of tile t = 2b + (0 for K, 1 for V) of the step's
@@ -266,7 +382,7 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
       for (int k = 0; k < P::kPerThread; ++k) {
         const int idx = tid + k * kPfThreads;
         const int t = idx / kTC, ci = idx % kTC;
-        const int blk = min(kSB * j + (t >> 1), nvis - 1);
+        const int blk = min(kSB * j + (t >> 1), kb1 - 1);
         const int64_t phys = sm_bt[blk - seg0];
         const u32x4* src = (const u32x4*)(((t & 1) ? vp : kp) + phys * blk_elems + head_off);
         dst[k] = src[ci];
@@ -279,7 +395,7 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
         const int idx = tid + k * kPfThreads;
         const int t = idx / kTC, ci = idx % kTC;
         const int b = t >> 1, blk = kSB * j + b;
-        u32x4 v = blk < nvis ? src[k] : u32x4{0, 0, 0, 0};
+        u32x4 v = blk < kb1 ? src[k] : u32x4{0, 0, 0, 0};
         if (t & 1) {
           if (blk * kBlock + kBlock > n) {
             // V of slots past the sequence end may be anything: zero it (tokens 4g'..4g'+3)
@@ -391,8 +507,8 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
     };
 
     // the block table goes through LDS in segments of kPfTableMax blocks; steps j in [js, je)
-    for (; seg0 < nvis; seg0 += kPfTableMax) {
-      const int seg_n = min(kPfTableMax, nvis - seg0);
+    for (; seg0 < kb1; seg0 += kPfTableMax) {
+      const int seg_n = min(kPfTableMax, kb1 - seg0);
       for (int i = tid; i < seg_n; i += kPfThreads) sm_bt[i] = btr[seg0 + i];
       __syncthreads();
       const int js = seg0 / kSB, je = (seg0 + seg_n + kSB - 1) / kSB;
@@ -418,12 +534,79 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
       const float lsum = accl[ct][0];
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // nothing visible -> zeros
       const int col = (w * kCT + ct) * 16 + c;
-      if (tq0 + col / G < tq_end && (lim[ct] >= 0 || n <= 0)) {
-        const int64_t o = ((int64_t)(qb + tq0 + col / G) * hq + h * G + col % G) * D + 4 * g;
+      if (item.slot < 0) {
+        if (tq0 + col / G < tq_end && (lim[ct] >= 0 || n <= 0)) {
+          const int64_t o = ((int64_t)(qb + tq0 + col / G) * hq + h * G + col % G) * D + 4 * g;
 #pragma unroll
-        for (int nn = 0; nn < Gm::kN; ++nn) store4<DT>(out, o + nn * 16, acc[ct][nn] * inv);
+          for (int nn = 0; nn < Gm::kN; ++nn) store4<DT>(out, o + nn * 16, acc[ct][nn] * inv);
+        }
+      } else if (tq0 + col / G < tq_end) {
+        // a piece: (m, l, o) of the column over this piece's keys; a column that sees
+        // none of them leaves (-inf, 0, 0), which the merge weighs 0
+        const int64_t row = (int64_t)item.slot * kPfSlotCols + col;
+#pragma unroll
+        for (int nn = 0; nn < Gm::kN; ++nn)
+          *(f32x4*)(part_o + row * D + nn * 16 + 4 * g) = acc[ct][nn] * inv;
+        if (g == 0) part_ml[row] = float2{lsum > 0.f ? m[ct] : -INFINITY, lsum};
       }
     }
+  }
+}
+
+// Merge of split items, one workgroup per (entry of the plan's merge list,
+// group of kMergeCols columns):
+//   o = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// A thread owns four consecutive dims of one column and loads eight pieces at
+// a time.
+constexpr int kMergeCols = 32;
+template <class DT, int D, int G>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(
+    typename DT::T* __restrict__ out, const float* __restrict__ part_o,
+    const float2* __restrict__ part_ml, int num_kv_heads, const PfMerge* __restrict__ merges,
+    const int32_t* __restrict__ queue) {
+  constexpr int kBatch = 8;
+  constexpr int QT = PfGeo<DT, D>::kCols / G;  // query tokens per q-tile
+  constexpr int kQuads = D / 4;
+  constexpr int kGroups = kPfSlotCols / kMergeCols;
+  const int j = xcd_unit(blockIdx.x, queue[2] * kGroups);
+  if (j < 0) return;
+  const PfMerge mg = merges[j / kGroups];
+  const int c0 = (j % kGroups) * kMergeCols;
+  const int hq = num_kv_heads * G;
+  const int tq0 = mg.qtile * QT;
+  const int ncols = min((min(mg.q_len, tq0 + QT) - tq0) * G - c0, kMergeCols);
+  for (int u = threadIdx.x; u < ncols * kQuads; u += blockDim.x) {
+    const int col = c0 + u / kQuads, d = (u % kQuads) * 4;
+    float M = -INFINITY, den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < mg.np; p0 += kBatch) {
+      float2 ml[kBatch];
+      f32x4 op[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int p = min(p0 + k, mg.np - 1);  // past the end: re-read the last (weight 0)
+        const int64_t row = (int64_t)(mg.slot0 + p) * kPfSlotCols + col;
+        ml[k] = part_ml[row];
+        op[k] = *(const f32x4*)(part_o + row * D + d);
+      }
+      float bm = M;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) bm = fmaxf(bm, ml[k].x);
+      const float bmu = bm == -INFINITY ? 0.f : bm;  // no key seen yet in any piece
+      const float f0 = fast_exp2(M - bmu);
+      num *= f0;
+      den *= f0;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        // pieces that hide the column (m = -inf, l = 0) weigh 0
+        const float f = p0 + k < mg.np ? fast_exp2(ml[k].x - bmu) * ml[k].y : 0.f;
+        num += f * op[k];
+        den += f;
+      }
+      M = bm;
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    store4<DT>(out, ((int64_t)(mg.qb + tq0 + col / G) * hq + mg.h * G + col % G) * D + d, num * inv);
   }
 }
 
@@ -455,15 +638,27 @@ static int tiled_launch(const AttnArgs& a) {
       return PKV_ERR_HIP;
     grid = cus * (per > 0 ? per : 1);
   }
-  PfItem* items = (PfItem*)a.ws_pf;
-  int32_t* queue = (int32_t*)((char*)a.ws_pf + a.pf_items * sizeof(PfItem));
+  const PfLayout L(a.pf_items, a.pf_slots, D);
+  PfItem* items = (PfItem*)((char*)a.ws_pf + L.items);
+  int2* tiles = (int2*)((char*)a.ws_pf + L.tiles);
+  PfMerge* merges = (PfMerge*)((char*)a.ws_pf + L.merges);
+  int32_t* queue = (int32_t*)((char*)a.ws_pf + L.queue);
+  float* part_o = (float*)((char*)a.ws_pf + L.part_o);
+  float2* part_ml = (float2*)((char*)a.ws_pf + L.part_ml);
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
                      a.num_seqs, a.num_kv_heads, G, P::kCols,
-                     small_chunk_max_cols(DT::kBytes == 2 ? PKV_BF16 : PKV_F32, D), items, queue,
-                     (int)a.pf_items);
+                     small_chunk_max_cols(DT::kBytes == 2 ? PKV_BF16 : PKV_F32, D), a.bt_stride,
+                     P::kSB, grid < kPfSplitWorkers ? grid : kPfSplitWorkers, (int)a.pf_slots,
+                     items, tiles, merges, queue, (int)(a.pf_items + a.pf_slots));
   hipLaunchKernelGGL((prefill_tiled_kernel<DT, D, G>), dim3(grid), dim3(kPfThreads), P::kLdsBytes,
                      a.stream, (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt,
-                     a.bt_stride, a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, items, queue);
+                     a.bt_stride, a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, items, queue,
+                     part_o, part_ml);
+  if (a.pf_slots >= 2) {  // split items, if the plan made any: at most pf_slots / 2 merges
+    const int64_t mgrid = (a.pf_slots / 2 * (kPfSlotCols / kMergeCols) + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((prefill_merge_kernel<DT, D, G>), dim3((unsigned)mgrid), dim3(256), 0,
+                       a.stream, (T*)a.out, part_o, part_ml, a.num_kv_heads, merges, queue);
+  }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -524,8 +719,16 @@ int64_t prefill_items_bound(int64_t num_seqs, int64_t num_q_tokens, int64_t num_
   return (num_q_tokens * num_q_heads + 127) / 128 + (chunks + 1) * num_q_heads;
 }
 
-int64_t prefill_workspace_bytes(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads) {
-  return prefill_items_bound(num_seqs, num_q_tokens, num_q_heads) * (int64_t)sizeof(PfItem) + 64;
+int64_t prefill_slots_bound(int64_t num_seqs, int64_t num_q_tokens) {
+  // every row has a query token, so a batch without more tokens than rows has no chunk
+  return num_q_tokens > num_seqs ? kPfMaxSlots : 0;
+}
+
+int64_t prefill_workspace_bytes(int64_t num_seqs, int64_t num_q_tokens, int64_t num_q_heads,
+                                int64_t head_dim) {
+  const PfLayout L(prefill_items_bound(num_seqs, num_q_tokens, num_q_heads),
+                   prefill_slots_bound(num_seqs, num_q_tokens), head_dim);
+  return L.total;
 }
 
 }  // namespace pkv

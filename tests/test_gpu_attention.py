@@ -243,6 +243,40 @@ def test_verify_full_size_sampled():
     assert np.array_equal(bits, run.out_bits())
 
 
+# Few long items: the tiled prefill cuts their context into pieces whose partials
+# a merge kernel combines.  A chunk of 100-300 tokens over 5,000-20,000 cached
+# tokens (a prompt's later chunk, or the new tokens after a prefix-cache hit),
+# alone or beside decode rows, with piece boundaries before, inside and after
+# the chunk's own tokens.
+@pytest.mark.parametrize("dtype,hq,hkv,d", [
+    ("bf16", 32, 8, 128), ("f16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 16, 2, 256),
+    ("bf16", 64, 8, 64),
+])
+def test_prefill_split_long_context(dtype, hq, hkv, d):
+    ctx = np.array([20000, 7, 5000, 12345], dtype=np.int64)
+    q = np.array([300, 1, 129, 100], dtype=np.int64)
+    spec = workloads.make_spec(f"pfs-{hq}-{hkv}-{d}", (446, 103, hq, hkv, d), dtype, hq, hkv, d, ctx, q)
+    _check(spec, f"split prefill {dtype} {hq}/{hkv} d{d}")
+
+
+def test_prefill_split_deterministic_and_placement_invariant():
+    import torch
+
+    gp = _gp()
+    ctx = np.array([9000, 3000], dtype=np.int64)
+    q = np.array([256, 64], dtype=np.int64)
+    spec = workloads.make_spec("pfs-det", (446, 104), "bf16", 32, 8, 128, ctx, q)
+    a = gp.prepare(spec)
+    first = a.out_bits().copy()
+    for _ in range(3):
+        gp.attention(a)
+        torch.cuda.synchronize()
+        assert np.array_equal(first, a.out_bits())
+    other = np.random.default_rng(79).permutation(spec.num_blocks).astype(np.int32)
+    b = gp.prepare(spec, free_order=other)
+    assert np.array_equal(first, b.out_bits())
+
+
 def _contiguous_pool(spec, gp):
     """Every sequence's tokens in one run of consecutive blocks (sequence order)."""
     import torch
