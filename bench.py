@@ -43,6 +43,17 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def unique_bytes(spec, tables):
+    """K/V bytes of the distinct physical blocks the batch reads (each shared block once),
+    plus Q, the output and the table entries: what HBM must deliver at the least."""
+    e = spec.elem_bytes
+    nb = -(-spec.seq_lens.astype(np.int64) // 16)
+    blocks = np.unique(np.concatenate([tables[s, :nb[s]] for s in range(spec.num_seqs)]))
+    kv = int(blocks.size) * spec.num_kv_heads * 16 * spec.head_dim * 2 * e
+    qo = spec.num_q_tokens * spec.num_q_heads * spec.head_dim * e * 2
+    return kv + qo + int(nb.sum()) * 4
+
+
 def algorithmic_bytes(spec):
     """Bytes the method must move per paged_attention call (each KV element once
     per KV-head group, plus Q, the output and the block-table entries)."""
@@ -346,10 +357,14 @@ def main():
                                      num_q_heads=spec.num_q_heads, max_seq_len=max_n,
                                      scale=spec.scale, workspace=ws)
     else:
+        # the allocator knows whether some block has several users: then the rows are
+        # read so that sharers read shared blocks together
+        shared = args.placement == "random" and alloc.num_shared() > 0
+
         def attention():
             ops.paged_attention(cache, out, q, tables, seq_lens, qsl, num_q_heads=spec.num_q_heads,
                                 max_q_len=max_q, max_seq_len=max_n, scale=spec.scale,
-                                workspace=ws)
+                                workspace=ws, shared_prefixes=shared)
 
     def step(ev_a=None, ev_b=None):
         if step_pairs is not None:
@@ -442,6 +457,8 @@ def main():
             "step": "copy_blocks (CoW pairs, if any) + kv_cache_write + paged_attention",
             "placement": args.placement,
             "kernel": args.kernel,
+            "shared_prefix_hint": bool(args.kernel == "paged" and args.placement == "random"
+                                       and alloc.num_shared() > 0),
         },
         "tokens_per_s": round(spec.num_q_tokens / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(int(spec.seq_lens.sum()) / (ms_step * 1e-3), 1),
@@ -462,6 +479,12 @@ def main():
             "avg_launch_us": round(attn_avg * 1e3, 2),
         },
     }
+    if args.placement == "random" and alloc.num_shared() > 0:
+        # rows share blocks: the algorithmic bytes count a shared block once per row that
+        # reads it; the distinct blocks are what HBM must deliver
+        ub = unique_bytes(spec, tables.cpu().numpy())
+        result["roofline"]["unique_bytes_per_launch"] = ub
+        result["roofline"]["unique_GBps"] = round(ub / (attn_avg * 1e-3) / 1e9, 2)
     torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(spec, host_bits(out, spec.dtype), args.cpu_seconds)

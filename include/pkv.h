@@ -136,6 +136,7 @@ int pkv_copy_blocks(const pkv_cache_t* cache, const int32_t* pairs, int32_t num_
  *   max_q_len, max_seq_len   host-known upper bounds over the batch
  *   scale          softmax scale applied to q.k (usually 1/sqrt(head_dim))
  *   workspace      device scratch of at least pkv_paged_attention_workspace_bytes()
+ *   flags          0, or PKV_ATTN_SHARED_PREFIXES (below)
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).  Preconditions
  * (not checked on the device): 1 <= q_len <= seq_len <= max_seq_len,
  * q_len <= max_q_len, ceil(seq_len/16) <= bt_stride, table entries < num_blocks.
@@ -147,7 +148,15 @@ int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void* out, cons
                         const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_tokens,
                         int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads, float scale,
-                        void* workspace, size_t workspace_bytes, void* stream);
+                        void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* flags of pkv_paged_attention (any other bit: PKV_ERR_INVALID_ARGUMENT).
+ * PKV_ATTN_SHARED_PREFIXES: rows share prefixes of blocks (parallel samples or
+ *   beam candidates that point at the same blocks, prefix-cache hits; [blog]
+ *   copy-on-write section).  A hint about speed only, never about results: the
+ *   work is then ordered so that rows read shared blocks at about the same time
+ *   (pkv_ba_num_shared() > 0 tells a caller that some block has several users). */
+#define PKV_ATTN_SHARED_PREFIXES 1u
 
 /*
  * contiguous_attention: the baseline the pages compare paging against -- every
@@ -290,6 +299,11 @@ int pkv_seq_cache_seal(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens,
 
 /* Blocks currently in the cache (in use or free). */
 int32_t pkv_ba_num_cached(const pkv_ba_t* ba);
+
+/* Blocks with a reference count of two or more: blocks that several sequences
+ * share after a fork or a prefix-cache hit ([devpress] "how memory is shared").
+ * -1 for a NULL handle. */
+int32_t pkv_ba_num_shared(const pkv_ba_t* ba);
 
 #ifdef __cplusplus
 }

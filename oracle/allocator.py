@@ -234,6 +234,11 @@ class BlockAllocatorModel:
     def num_cached(self) -> int:
         return len(self._cache()[0])
 
+    def num_shared(self) -> int:
+        """Blocks that several sequences use (devpress page, how memory is shared):
+        a reference count of two or more."""
+        return sum(1 for r in self.ref if r >= 2)
+
     # ---- statistics ---------------------------------------------------------
     @staticmethod
     def tail_waste(n: int) -> int:

@@ -31,6 +31,7 @@ EXPORTS = (
     "pkv_ba_num_free", "pkv_ba_num_blocks", "pkv_blocks_for_tokens", "pkv_seq_append_slots",
     "pkv_batch_append_slots", "pkv_seq_make_writable", "pkv_seq_fork", "pkv_seq_free",
     "pkv_prefix_hash", "pkv_seq_cache_lookup", "pkv_seq_cache_seal", "pkv_ba_num_cached",
+    "pkv_ba_num_shared",
 )
 
 
@@ -73,7 +74,7 @@ def load() -> ctypes.CDLL:
         "pkv_kv_cache_write": (ctypes.c_int, [pcache, i32, P, P, P, i32, P]),
         "pkv_copy_blocks": (ctypes.c_int, [pcache, P, i32, P]),
         "pkv_paged_attention": (ctypes.c_int, [pcache, i32, P, P, P, i32, P, P, i32, i32, i32, i32,
-                                               i32, f32, P, sz, P]),
+                                               i32, f32, P, sz, ctypes.c_uint32, P]),
         "pkv_contiguous_attention": (ctypes.c_int, [pcache, i32, P, P, P, P, P, i32, i32, i32, i32,
                                                     f32, P, sz, P]),
         "pkv_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -96,6 +97,7 @@ def load() -> ctypes.CDLL:
         "pkv_seq_cache_lookup": (ctypes.c_int, [P, pi32, i32, pi32, i32, pi32]),
         "pkv_seq_cache_seal": (ctypes.c_int, [P, pi32, i32, pi32, i32]),
         "pkv_ba_num_cached": (i32, [P]),
+        "pkv_ba_num_shared": (i32, [P]),
     }
     for name in EXPORTS:
         fn = getattr(lib, name)

@@ -133,6 +133,10 @@ class BlockAllocator:
     def num_cached(self) -> int:
         return int(self._lib.pkv_ba_num_cached(self._h))
 
+    def num_shared(self) -> int:
+        """Blocks with a reference count of two or more."""
+        return int(self._lib.pkv_ba_num_shared(self._h))
+
 
 def prefix_hash(parent: int, tokens16) -> int:
     t = np.ascontiguousarray(tokens16, dtype=np.int32)

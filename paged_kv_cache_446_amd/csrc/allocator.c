@@ -36,6 +36,7 @@ struct pkv_ba {
   int32_t* prev;
   int32_t head, tail; /* front and back of the free queue (-1 if empty) */
   int32_t count;      /* number of free blocks */
+  int32_t num_shared; /* blocks with a count of 2 or more */
   /* prefix cache */
   uint8_t* sealed;   /* [num_blocks] 1 if the block is in the cache */
   uint64_t* hash;    /* [num_blocks] chained hash of the block's tokens */
@@ -200,6 +201,14 @@ void pkv_ba_destroy(pkv_ba_t* ba) {
 
 static int valid_id(const pkv_ba_t* ba, int32_t b) { return b >= 0 && b < ba->num_blocks; }
 
+/* every count change of an allocated block goes through these two */
+static void ref_inc(pkv_ba_t* ba, int32_t b) {
+  if (++ba->ref[b] == 2) ba->num_shared++;
+}
+static void ref_dec(pkv_ba_t* ba, int32_t b) {
+  if (ba->ref[b]-- == 2) ba->num_shared--;
+}
+
 int pkv_ba_alloc(pkv_ba_t* ba, int32_t* block) {
   if (!ba || !block) return PKV_ERR_INVALID_ARGUMENT;
   if (ba->count == 0) return PKV_ERR_OUT_OF_BLOCKS;
@@ -213,14 +222,15 @@ int pkv_ba_incref(pkv_ba_t* ba, int32_t block) {
   if (!ba || !valid_id(ba, block)) return PKV_ERR_INVALID_ARGUMENT;
   if (ba->ref[block] <= 0) return PKV_ERR_REFCOUNT;
   if (ba->ref[block] == INT32_MAX) return PKV_ERR_REFCOUNT;
-  ba->ref[block]++;
+  ref_inc(ba, block);
   return PKV_OK;
 }
 
 int pkv_ba_decref(pkv_ba_t* ba, int32_t block) {
   if (!ba || !valid_id(ba, block)) return PKV_ERR_INVALID_ARGUMENT;
   if (ba->ref[block] <= 0) return PKV_ERR_REFCOUNT;
-  if (--ba->ref[block] == 0) q_push_back(ba, block);
+  ref_dec(ba, block);
+  if (ba->ref[block] == 0) q_push_back(ba, block);
   return PKV_OK;
 }
 
@@ -328,7 +338,7 @@ int pkv_seq_fork(pkv_ba_t* ba, const int32_t* src_table, int32_t nblk, int32_t* 
   for (int32_t j = 0; j < nblk; ++j)
     if (ba->ref[src_table[j]] == INT32_MAX) return PKV_ERR_REFCOUNT;
   for (int32_t j = 0; j < nblk; ++j) {
-    ba->ref[src_table[j]]++;
+    ref_inc(ba, src_table[j]);
     dst_table[j] = src_table[j];
   }
   return PKV_OK;
@@ -349,7 +359,7 @@ int pkv_seq_free(pkv_ba_t* ba, const int32_t* table, int32_t nblk) {
   while (--j >= 0) {
     const int32_t b = table[j];
     if (ba->ref[b] == 0) q_pop_back(ba);
-    ba->ref[b]++;
+    ref_inc(ba, b);
   }
   return rc;
 }
@@ -370,7 +380,7 @@ int pkv_seq_cache_lookup(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens
     const int32_t b = find_sealed(ba, h, j ? table[j - 1] : -1, tk);
     if (b < 0 || ba->ref[b] == INT32_MAX) break;
     if (ba->ref[b] == 0) q_remove(ba, b); /* a cached block back from the free queue */
-    ba->ref[b]++;
+    ref_inc(ba, b);
     table[j] = b;
   }
   *nblk = j;
@@ -409,3 +419,5 @@ int pkv_seq_cache_seal(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens,
 }
 
 int32_t pkv_ba_num_cached(const pkv_ba_t* ba) { return ba ? ba->num_sealed : -1; }
+
+int32_t pkv_ba_num_shared(const pkv_ba_t* ba) { return ba ? ba->num_shared : -1; }

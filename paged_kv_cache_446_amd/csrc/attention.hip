@@ -38,6 +38,7 @@
 namespace pkv {
 
 constexpr int kPartBlocks = 64;  // blocks per decode partition (1024 tokens)
+constexpr int kPlanLevels = 2048;  // partition indices the plan orders items by (2M tokens)
 
 // ---------------------------------------------------------------------------
 // Decode and short chunks: a 1-D grid over (item, KV head), 4 wavefronts each.
@@ -67,13 +68,17 @@ struct alignas(16) DecodeItem {
 };
 
 // Work lists of one call, written by decode_plan_kernel: the items of one-tile
-// rows (class 1) and of two-tile rows (class 2), each in sequence order, with
-// h = 0.  Workgroup units are (item, KV head) pairs, item-major, dealt to the
-// eight XCDs in contiguous runs (xcd_unit), so the KV heads of a partition and
-// neighbouring partitions share an XCD.  Sequences split over several
-// partitions own workspace rows from base[s]: row base[s] + (p * q_len + t) * Hq
-// + head holds partition p's result for query token t; one merge entry per
-// (split sequence, query token).
+// rows (class 1) and of two-tile rows (class 2), with h = 0, in sequence order,
+// or partition-major when the caller says that rows share prefixes of blocks
+// (PKV_ATTN_SHARED_PREFIXES): partition 0 of every row, then partition 1 of
+// every row that has one, and so on (sequence order within a partition index is
+// not kept).  Rows that share blocks then read them at about the same time, on
+// the same XCD, so its L2 serves most of those reads; without sharing, sequence
+// order spreads long and short rows evenly over the XCDs.  Workgroup units are
+// (item, KV head) pairs, item-major, dealt to the eight XCDs in contiguous runs
+// (xcd_unit).  Sequences split over several partitions own workspace rows from
+// base[s]: row base[s] + (p * q_len + t) * Hq + head holds partition p's result
+// for query token t; one merge entry per (split sequence, query token).
 // One merge: the output query row, the partition count, the workspace row of
 // (partition 0, this token, head 0) and the rows between partitions.
 struct MergeEntry {
@@ -89,6 +94,7 @@ struct DecodePlan {
   int64_t* base;      // [num_seqs]
   int num_seqs;
   int cap;            // num_seqs * max_parts
+  int head_major;     // units ordered (KV head, item) instead of (item, KV head)
 };
 
 // Blocks per partition of a row: 1024 tokens for decode rows; a multi-token row
@@ -117,15 +123,28 @@ __device__ __forceinline__ int row_class(int q_len, int max_q, int G, int max_co
 __global__ __launch_bounds__(1024) void decode_plan_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int num_seqs,
     int bt_stride, int max_parts, int max_q, int G, int max_cols, int hq, long long budget,
-    DecodePlan plan) {
+    int order_by_part, DecodePlan plan) {
   __shared__ int sm_tot[3][1024 / kWave];
   __shared__ long long sm_rows[1024 / kWave];
+  __shared__ int sm_lvl[2][kPlanLevels];  // items per partition index, then cursors
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nwaves = blockDim.x / kWave;
   const int k = (num_seqs + blockDim.x - 1) / blockDim.x;
   const int s0 = tid * k;
   auto blocks = [&](int n) {
     return n > 0 ? min((n + kBlock - 1) / kBlock, min(bt_stride, max_parts * kPartBlocks)) : 0;
   };
+  // One row per thread (up to 1024 rows): the row's metadata is loaded once.
+  int c_qb = 0, c_qe = 0, c_n = 0;
+  if (k == 1 && s0 < num_seqs) {
+    c_qb = qsl[s0];
+    c_qe = qsl[s0 + 1];
+    c_n = seq_lens[s0];
+  }
+  auto qb_of = [&](int s) { return k == 1 ? c_qb : qsl[s]; };
+  auto qlen_of = [&](int s) { return k == 1 ? c_qe - c_qb : qsl[s + 1] - qsl[s]; };
+  auto n_of = [&](int s) { return k == 1 ? c_n : seq_lens[s]; };
+  const int levels = max_parts < kPlanLevels ? max_parts : kPlanLevels;
+  for (int i = tid; i < 2 * levels; i += blockDim.x) sm_lvl[i / levels][i % levels] = 0;
   int shift = 0, n1, n2, nmg, x1, x2, xm;
   long long nrow, xr, trow;
   for (;; ++shift) {
@@ -134,10 +153,10 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
     for (int j = 0; j < k; ++j) {
       const int s = s0 + j;
       if (s >= num_seqs) break;
-      const int q_len = qsl[s + 1] - qsl[s];
+      const int q_len = qlen_of(s);
       const int cls = row_class(q_len, max_q, G, max_cols);
       if (!cls) continue;
-      const int n = seq_lens[s], pb = part_blocks(q_len, shift);
+      const int n = n_of(s), pb = part_blocks(q_len, shift);
       const int np = n > 0 ? (blocks(n) + pb - 1) / pb : 1;
       (cls == 1 ? n1 : n2) += np;
       if (np > 1) {
@@ -185,19 +204,49 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
   }
   int p1 = b1 + x1 - n1, p2 = b2 + x2 - n2, pm = bm + xm - nmg;
   long long pr = br + xr - nrow;
+  // partition-major lists: items per partition index, their starts, then cursors
+  const bool by_part = order_by_part && max_parts <= kPlanLevels;
+  if (by_part) {
+    for (int j = 0; j < k; ++j) {
+      const int s = s0 + j;
+      if (s >= num_seqs) break;
+      const int q_len = qlen_of(s);
+      const int cls = row_class(q_len, max_q, G, max_cols);
+      if (!cls) continue;
+      const int n = n_of(s), pb = part_blocks(q_len, shift);
+      const int np = n > 0 ? (blocks(n) + pb - 1) / pb : 1;
+      for (int p = 0; p < np; ++p) atomicAdd(&sm_lvl[cls - 1][p], 1);
+    }
+    __syncthreads();
+    if (tid < 2) {  // exclusive scan over the partition indices of one class
+      int run = 0;
+      for (int p = 0; p < max_parts; ++p) {
+        const int c = sm_lvl[tid][p];
+        sm_lvl[tid][p] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+  }
   for (int j = 0; j < k; ++j) {
     const int s = s0 + j;
     if (s >= num_seqs) break;
-    const int q_len = qsl[s + 1] - qsl[s];
+    const int q_len = qlen_of(s);
     const int cls = row_class(q_len, max_q, G, max_cols);
     if (!cls) continue;
-    const int n = seq_lens[s], nb = blocks(n), pb = part_blocks(q_len, shift);
+    const int n = n_of(s), nb = blocks(n), pb = part_blocks(q_len, shift);
     const int np = n > 0 ? (nb + pb - 1) / pb : 1;
-    const int qb = qsl[s];
+    const int qb = qb_of(s);
     DecodeItem* rec = plan.items + (cls == 1 ? (int64_t)p1 : (int64_t)plan.cap + p2);
-    for (int p = 0; p < np; ++p)
-      rec[p] = DecodeItem{s, 0, p * pb, min(nb, (p + 1) * pb), qb, q_len, n, p,
-                          np > 1 ? pr + (long long)p * q_len * hq : -1, 0};
+    DecodeItem* list = plan.items + (cls == 1 ? 0 : (int64_t)plan.cap);
+    for (int p = 0; p < np; ++p) {
+      const DecodeItem d{s, 0, p * pb, min(nb, (p + 1) * pb), qb, q_len, n, p,
+                         np > 1 ? pr + (long long)p * q_len * hq : -1, 0};
+      if (by_part)
+        list[atomicAdd(&sm_lvl[cls - 1][p], 1)] = d;
+      else
+        rec[p] = d;
+    }
     (cls == 1 ? p1 : p2) += np;
     if (np > 1) {
       for (int t = 0; t < q_len; ++t)
@@ -229,12 +278,16 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
   // and are not merged into one load after the paths join.
   DecodeItem it;
   if (plan.counts) {
-    const int j = xcd_unit(blockIdx.x, plan.counts[CT == 1 ? 0 : 2] * num_kv_heads);
+    const int live = plan.counts[CT == 1 ? 0 : 2];
+    const int j = xcd_unit(blockIdx.x, live * num_kv_heads);
     if (j < 0) return;
-    it = plan.items[(CT == 1 ? 0 : (int64_t)plan.cap) + j / num_kv_heads];
+    // units item-major (the KV heads of an item together), or head-major for rows that
+    // share blocks (the rows reading one (block, head) tile run together)
+    const int i = plan.head_major ? j % live : j / num_kv_heads;
+    it = plan.items[(CT == 1 ? 0 : (int64_t)plan.cap) + i];
     asm volatile("" : "+s"(it.s), "+s"(it.b0), "+s"(it.b1), "+s"(it.qb), "+s"(it.q_len),
                  "+s"(it.n), "+s"(it.part), "+s"(it.wrow));
-    it.h = j % num_kv_heads;
+    it.h = plan.head_major ? j / live : j % num_kv_heads;
     if (it.wrow >= 0) it.wrow += it.h * G;
   } else {  // one partition per row: every sequence is an item
     const int j = xcd_unit(blockIdx.x, plan.num_seqs * num_kv_heads);
@@ -471,6 +524,7 @@ static int launch(const AttnArgs& a) {
   DecodePlan plan;
   plan.num_seqs = a.num_seqs;
   plan.cap = a.num_seqs * a.max_parts;
+  plan.head_major = a.order_by_part ? 1 : 0;
   plan.counts = nullptr;
   plan.items = nullptr;
   plan.merge = nullptr;
@@ -485,7 +539,8 @@ static int launch(const AttnArgs& a) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
                        a.num_seqs, a.bt_stride, a.max_parts, a.max_q_len, G, kMaxCols,
                        a.num_kv_heads * G,
-                       (long long)split_rows(a.num_seqs, a.max_parts, a.num_kv_heads * G), plan);
+                       (long long)split_rows(a.num_seqs, a.max_parts, a.num_kv_heads * G),
+                       a.order_by_part ? 1 : 0, plan);
   }
   // a class no row can be in is not launched: two-tile rows need max_q_len * G > 16,
   // and rows of one q_len are all in the same class
@@ -555,8 +610,9 @@ static int attention_impl(const pkv_cache_t* cache, int32_t layer, void* out, co
                           const int32_t* seq_lens, const int32_t* query_start_loc,
                           int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
                           int32_t max_seq_len, int32_t num_q_heads, float scale, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, uint32_t flags, void* stream) {
   int rc = check_cache(cache);
+  if (flags & ~PKV_ATTN_SHARED_PREFIXES) return PKV_ERR_INVALID_ARGUMENT;
   if (rc != PKV_OK) return rc;
   if (layer < 0 || layer >= cache->num_layers) return PKV_ERR_INVALID_ARGUMENT;
   if (num_seqs < 0 || num_q_tokens < 0 || max_q_len < 0 || max_seq_len < 0 || bt_stride < 0)
@@ -599,6 +655,7 @@ static int attention_impl(const pkv_cache_t* cache, int32_t layer, void* out, co
   a.max_q_len = max_q_len;
   a.max_parts = (int)max_partitions(max_seq_len);
   a.uniform_q = (int64_t)num_seqs * max_q_len == num_q_tokens;
+  a.order_by_part = (flags & PKV_ATTN_SHARED_PREFIXES) != 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   const int64_t rows = split_rows(num_seqs, a.max_parts, num_q_heads);
   a.ws_ml = (float*)workspace;
@@ -630,10 +687,11 @@ extern "C" int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void
                                    const int32_t* seq_lens, const int32_t* query_start_loc,
                                    int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
                                    int32_t max_seq_len, int32_t num_q_heads, float scale,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+                                   void* workspace, size_t workspace_bytes, uint32_t flags,
+                                   void* stream) {
   return attention_impl(cache, layer, out, q, block_tables, bt_stride, 0, seq_lens,
                         query_start_loc, num_seqs, num_q_tokens, max_q_len, max_seq_len,
-                        num_q_heads, scale, workspace, workspace_bytes, stream);
+                        num_q_heads, scale, workspace, workspace_bytes, flags, stream);
 }
 
 extern "C" int pkv_contiguous_attention(const pkv_cache_t* cache, int32_t layer, void* out,
@@ -646,5 +704,5 @@ extern "C" int pkv_contiguous_attention(const pkv_cache_t* cache, int32_t layer,
   const int32_t run = (int32_t)(((int64_t)max_seq_len + kBlock - 1) / kBlock);
   return attention_impl(cache, layer, out, q, first_block, run > 0 ? run : 1, 1, seq_lens,
                         query_start_loc, num_seqs, num_q_tokens, 1, max_seq_len, num_q_heads,
-                        scale, workspace, workspace_bytes, stream);
+                        scale, workspace, workspace_bytes, 0, stream);
 }

@@ -222,6 +222,7 @@ struct AttnArgs {
   const int32_t* qsl;
   int num_seqs, num_kv_heads, max_q_len, max_parts;
   bool uniform_q;     // every row has max_q_len query tokens (num_q_tokens = num_seqs * max_q_len)
+  bool order_by_part; // rows share prefixes of blocks: decode work partition-major
   float scale_log2;
   float* ws_o;
   float* ws_ml;

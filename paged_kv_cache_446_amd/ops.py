@@ -72,7 +72,9 @@ def workspace_bytes(num_seqs, num_q_tokens, max_seq_len, num_q_heads, head_dim) 
 
 def paged_attention(cache: PagedCache, out, q, block_tables, seq_lens, query_start_loc, *,
                     num_q_heads: int, max_q_len: int, max_seq_len: int, scale: float,
-                    workspace, layer: int = 0, stream=None):
+                    workspace, layer: int = 0, shared_prefixes: bool = False, stream=None):
+    """shared_prefixes: rows share prefixes of blocks (a speed hint; results are the
+    same either way)."""
     lib = _lib.load()
     for t, dt in ((block_tables, torch.int32), (seq_lens, torch.int32), (query_start_loc, torch.int32)):
         assert t.dtype == dt and t.is_contiguous() and t.is_cuda
@@ -83,7 +85,8 @@ def paged_attention(cache: PagedCache, out, q, block_tables, seq_lens, query_sta
                                        _ptr(block_tables), block_tables.shape[-1], _ptr(seq_lens),
                                        _ptr(query_start_loc), S, Tq, max_q_len, max_seq_len,
                                        num_q_heads, float(scale), _ptr(workspace),
-                                       workspace.numel() * workspace.element_size(), _stream(stream)),
+                                       workspace.numel() * workspace.element_size(),
+                                       1 if shared_prefixes else 0, _stream(stream)),
                "pkv_paged_attention")
 
 

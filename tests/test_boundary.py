@@ -51,13 +51,16 @@ def test_host_side_argument_checks_without_gpu():
     assert lib.pkv_copy_blocks(ctypes.byref(bad), None, 1, None) == -1
     unsup = L.CacheDesc(16, 16, 1, 8, 8, 96, 2)  # head_dim 96 is not built
     assert lib.pkv_paged_attention(ctypes.byref(unsup), 0, 16, 16, 16, 8, 16, 16, 1, 1, 1, 16, 32,
-                                   0.1, 16, 1 << 20, None) == -2
+                                   0.1, 16, 1 << 20, 0, None) == -2
     ok = L.CacheDesc(16, 16, 1, 8, 8, 128, 2)
     # group size 3 is unsupported; workspace too small is reported as such
     assert lib.pkv_paged_attention(ctypes.byref(ok), 0, 16, 16, 16, 8, 16, 16, 1, 1, 1, 16, 24,
-                                   0.1, 16, 1 << 20, None) == -2
+                                   0.1, 16, 1 << 20, 0, None) == -2
     assert lib.pkv_paged_attention(ctypes.byref(ok), 0, 16, 16, 16, 8, 16, 16, 1, 1, 1, 16, 32,
-                                   0.1, 16, 8, None) == -5
+                                   0.1, 16, 8, 0, None) == -5
+    # flags other than PKV_ATTN_SHARED_PREFIXES are rejected
+    assert lib.pkv_paged_attention(ctypes.byref(ok), 0, 16, 16, 16, 8, 16, 16, 1, 1, 1, 16, 32,
+                                   0.1, 16, 1 << 20, 2, None) == -1
     assert lib.pkv_paged_attention_workspace_bytes(256, 256, 8192, 32, 128) > 0
 
 

@@ -277,6 +277,28 @@ def test_prefill_split_deterministic_and_placement_invariant():
     assert np.array_equal(first, b.out_bits())
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("c4", dict(num_seqs=12, max_len=300, variant=6, prefix=2500)),
+    ("c3", dict(num_seqs=24, max_len=3000, variant=6)),
+    ("c5", dict(num_seqs=12, max_len=1500, variant=6)),
+])
+def test_shared_prefix_hint_changes_no_bits(name, kw):
+    # the hint only reorders the work (rows that share blocks read them together)
+    import torch
+
+    gp = _gp()
+    spec = workloads.scaled_spec(name, **kw)
+    run = gp.prepare(spec, run_attention=False)
+    gp.attention(run, shared_prefixes=False)
+    torch.cuda.synchronize()
+    plain = run.out_bits().copy()
+    gp.attention(run, shared_prefixes=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(plain, run.out_bits())
+    if name == "c4":
+        assert run.alloc.num_shared() > 0
+
+
 def _contiguous_pool(spec, gp):
     """Every sequence's tokens in one run of consecutive blocks (sequence order)."""
     import torch

@@ -80,7 +80,7 @@ def _random_requests(seed, alloc, n_ops=500, cap=48):
                 log.append(("finish", nb))
         except Exception as e:  # both sides must fail the same way
             log.append(("error", type(e).__name__ if not hasattr(e, "name") else e.name))
-        log.append(("state", alloc.num_free(), alloc.num_cached()))
+        log.append(("state", alloc.num_free(), alloc.num_cached(), alloc.num_shared()))
     return log
 
 
@@ -171,3 +171,28 @@ def test_prefix_hash_chains_parent_and_tokens():
     u[15] += 1
     assert prefix_hash(0, u) != h0                      # depends on every token
     assert prefix_hash(0, t[::-1].copy()) != h0         # and on their order
+
+
+@pytest.mark.parametrize("impl", ["c", "model"])
+def test_shared_block_count_follows_forks_cow_and_frees(impl):
+    # blocks several sequences point at (the devpress page's sharing section): a fork
+    # shares every block, copy-on-write of the partial last block unshares one, and
+    # freeing one sharer unshares the rest
+    a = _new_c(16, None) if impl == "c" else oalloc.BlockAllocatorModel(16)
+    t1 = a.new_table(8)
+    nb, ln, _, _ = a.append_slots(t1, 0, 0, 40)  # 3 blocks, the last holds 8 tokens
+    assert a.num_shared() == 0
+    t2 = a.fork(t1, nb)
+    assert a.num_shared() == 3
+    nb2, ln2, _, pairs = a.append_slots(t2, nb, ln, 1)  # CoW of the shared partial block
+    assert len(pairs) == 1 and a.num_shared() == 2
+    a.free_seq(t1, nb)
+    assert a.num_shared() == 0
+    t3 = a.fork(t2, nb2)
+    t4 = a.fork(t2, nb2)
+    assert a.num_shared() == 3  # counts of 3 are still one shared block each
+    a.free_seq(t3, nb2)
+    a.free_seq(t4, nb2)
+    a.free_seq(t2, nb2)
+    assert a.num_shared() == 0 and a.num_free() == 16
+
