@@ -35,6 +35,7 @@ WORKLOAD_NAMES = {
     "c4": "shared-prefix parallel sampling: 64 seqs share a 10000-token prefix + U[0,256] private tails, CoW, 32q/8kv, bf16",
     "c5": "mixed chunked-prefill + decode: 16 chunks q U[16,512] over context U[0,32768] + 128 decodes U[64,8192], 32q/8kv, bf16",
     "verify": "speculative-decoding verify: 256 seqs, context log-uniform [64,8192], k+1=5 query tokens each, 32q/8kv heads, head_dim 128, bf16",
+    "beam": "beam search: 64 requests x 4 candidates, prompts U[512,4096], each step a reorder + 1 token per candidate (copy-on-write of shared last blocks), 32q/8kv heads, head_dim 128, bf16",
     "prefix-cache": "repeated 10000-token prompt + 256 new tokens (second request), 32q/8kv heads, head_dim 128, bf16",
 }
 
@@ -256,6 +257,109 @@ def bench_prefix_cache(args):
     }), flush=True)
 
 
+def bench_beam(args):
+    """Beam search churn (blog page, beam search; copy-on-write section): every step
+    the candidates of each request continue random parents (pkv_seq_reorder), each
+    appends one token (copy-on-write of a shared, partly filled last block), then
+    copy_blocks + kv_cache_write + paged_attention run over all candidates.  value =
+    median host time of the reorder + appends + median GPU time of the three calls."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_446_amd import ops
+    from paged_kv_cache_446_amd.allocator import BlockAllocator
+    from tests.gpu_pipeline import dev_bits
+
+    dev = "cuda:0"
+    R, B, hq, hkv, D = 64, 4, 32, 8, 128
+    steps_total = args.warmup + args.steps
+    rng = np.random.default_rng([446, 70])
+    prompts = rng.integers(512, 4096, size=R, endpoint=True)
+    cap = int(-(-(prompts.max() + steps_total + 1) // 16)) + 1
+    num_blocks = int(2 * (-(-prompts // 16)).sum() + 2 * R * B * (-(-steps_total // 16) + 2))
+    alloc = BlockAllocator(num_blocks, free_order=rng.permutation(num_blocks).astype(np.int32))
+    kp = torch.zeros(num_blocks * hkv * 16 * D, dtype=torch.int16, device=dev)
+    vp = torch.zeros_like(kp)
+    cache = ops.PagedCache(kp, vp, hkv, D, dtype="bf16")
+    tables = np.full((R * B, cap), -1, np.int32)
+    nblk = np.zeros(R * B, np.int32)
+    lens = np.zeros(R * B, np.int32)
+    for r in range(R):  # the prompt once, its candidates forks of it
+        t = tables[r * B:(r + 1) * B]
+        nb, ln, slots, _ = alloc.append_slots(t[0], 0, 0, int(prompts[r]))
+        for b in range(1, B):
+            t[b] = alloc.fork(t[0], nb)
+        nblk[r * B:(r + 1) * B], lens[r * B:(r + 1) * B] = nb, ln
+        k = workloads.normal_bits((446, 71, r, 0), (len(slots), hkv, D), "bf16")
+        v = workloads.normal_bits((446, 71, r, 1), (len(slots), hkv, D), "bf16")
+        ops.kv_cache_write(cache, dev_bits(k, "bf16"), dev_bits(v, "bf16"), torch.from_numpy(slots).to(dev))
+    S = R * B
+    k_new = dev_bits(workloads.normal_bits((446, 72, 0), (S, hkv, D), "bf16"), "bf16")
+    v_new = dev_bits(workloads.normal_bits((446, 72, 1), (S, hkv, D), "bf16"), "bf16")
+    q = dev_bits(workloads.normal_bits((446, 72, 2), (S, hq, D), "bf16"), "bf16")
+    out = torch.zeros_like(q)
+    qsl = torch.arange(S + 1, dtype=torch.int32, device=dev)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    max_n = int(lens.max()) + steps_total + 1
+    ws = torch.empty(ops.workspace_bytes(S, S, max_n, hq, D), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    host_us, pairs_n, gpu_ms, copy_ms, attn_ms = [], [], [], [], []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for it in range(steps_total):
+        t0 = time.perf_counter()
+        # each candidate continues one of its own request's candidates (parents are row
+        # numbers of the whole batch: one native call reorders every request)
+        parents = (rng.integers(0, B, size=(R, B)) + (np.arange(R) * B)[:, None]).astype(np.int32)
+        alloc.reorder(tables, nblk, lens, parents.ravel())
+        slots, pairs = alloc.batch_append_slots(tables, nblk, lens, np.ones(S, np.int32))
+        dt = (time.perf_counter() - t0) * 1e6
+        d_slots = torch.from_numpy(slots).to(dev)
+        d_pairs = torch.from_numpy(pairs.copy()).to(dev) if len(pairs) else None
+        d_tables = torch.from_numpy(np.where(tables < 0, 0, tables)).to(dev)
+        d_lens = torch.from_numpy(lens.copy()).to(dev)
+        torch.cuda.synchronize()  # the step's uploads are done
+        # a short spin keeps the GPU busy while the host queues the step, so the
+        # events time the kernels, not the host's launch latency
+        torch.cuda._sleep(500_000)
+        ev[0].record()
+        if d_pairs is not None:
+            ops.copy_blocks(cache, d_pairs)
+        ev[1].record()
+        ops.kv_cache_write(cache, k_new, v_new, d_slots)
+        ev[2].record()
+        ops.paged_attention(cache, out, q, d_tables, d_lens, qsl, num_q_heads=hq, max_q_len=1,
+                            max_seq_len=max_n, scale=scale, workspace=ws,
+                            shared_prefixes=alloc.num_shared() > 0)
+        ev[3].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            host_us.append(dt)
+            pairs_n.append(len(pairs))
+            gpu_ms.append(ev[0].elapsed_time(ev[3]))
+            copy_ms.append(ev[0].elapsed_time(ev[1]))
+            attn_ms.append(ev[2].elapsed_time(ev[3]))
+    gpu_ms, copy_ms, attn_ms, host_med = (np.median(x) for x in (gpu_ms, copy_ms, attn_ms, host_us))
+    step_ms = float(gpu_ms) + float(host_med) / 1e3
+    log(f"{args.steps} steps: host {host_med:.0f} us, GPU {gpu_ms * 1e3:.0f} us (medians: "
+        f"copy_blocks {copy_ms * 1e3:.1f} us for {np.mean(pairs_n):.0f} pairs, attention "
+        f"{attn_ms * 1e3:.0f} us), shared blocks {alloc.num_shared()}")
+    pair_bytes = 2 * hkv * 16 * D * 2 * 2  # K and V of a block, read and written
+    print(json.dumps({
+        "metric": "beam search step: host reorder + append, then copy_blocks + kv_cache_write + "
+                  "paged_attention (one layer)",
+        "value": round(step_ms, 4), "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+        "host_us": round(float(host_med), 1), "gpu_us": round(float(gpu_ms) * 1e3, 1),
+        "cow_pairs_per_step": round(float(np.mean(pairs_n)), 1),
+        "copy_blocks_us": round(float(copy_ms) * 1e3, 2),
+        "copy_blocks_GBps": round(float(np.mean(pairs_n)) * pair_bytes / (float(copy_ms) * 1e-3) / 1e9, 1),
+        "attention_us": round(float(attn_ms) * 1e3, 1),
+        "shared_blocks": alloc.num_shared(),
+        "config": {"workload": WORKLOAD_NAMES["beam"], "requests": R, "beams": B, "num_q_heads": hq,
+                   "num_kv_heads": hkv, "head_dim": D, "block_size": 16},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +398,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.config == "prefix-cache":
         return bench_prefix_cache(args)
+    if args.config == "beam":
+        return bench_beam(args)
     dev = "cuda:0"
     spec = workloads.named_spec(args.config)
     log(f"workload {args.config}: S={spec.num_seqs} context tokens={int(spec.seq_lens.sum())} "

@@ -227,7 +227,10 @@ int64_t pkv_blocks_for_tokens(int64_t n, int32_t block_size);
  * caller must run pkv_copy_blocks on that pair before writing the slots.
  * New blocks follow in logical order.  All or nothing: on any error nothing
  * changes.  Errors: PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_INVALID_ARGUMENT (table
- * too small, inconsistent state), PKV_ERR_REFCOUNT (table holds a free block).
+ * too small, inconsistent state, last entry not a block id), PKV_ERR_REFCOUNT
+ * (the last block is free).  Only the last existing entry is read, so a call
+ * costs O(new blocks), not O(context); the whole table is checked by
+ * pkv_seq_fork, pkv_seq_reorder and pkv_seq_free.
  */
 int pkv_seq_append_slots(pkv_ba_t* ba, int32_t* table, int32_t cap, int32_t* nblk,
                          int32_t* seq_len, int32_t n_new, int64_t* slots_out, int32_t* cow_pair,
@@ -296,6 +299,24 @@ int pkv_seq_cache_lookup(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens
  * content is cached under another block stays out of the cache. */
 int pkv_seq_cache_seal(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens,
                        const int32_t* table, int32_t nblk);
+
+/*
+ * Beam reorder: after a beam-search step the surviving candidates continue some
+ * of the old rows, several children per parent or none ([blog] beam search: the
+ * candidates share their beginning; [devpress] "how memory is shared").  In
+ * place, for num_rows rows of tables [num_rows][cap], nblk and seq_lens: new row
+ * i becomes a copy of old row parents[i].  Every block of a parent gains one user
+ * per child (in child order), then every block of every old row loses one (in row
+ * order; a block left without users joins the free queue).  The next append to a
+ * row whose last block is shared and partly filled copies that block
+ * (pkv_seq_append_slots, copy-on-write).
+ *   parents  int32 [num_rows], each in [0, num_rows)
+ *   work     int32 scratch of num_rows * cap entries, owned by the caller
+ * Checks everything first: on an error nothing changes (PKV_ERR_INVALID_ARGUMENT,
+ * or PKV_ERR_REFCOUNT if a count would overflow or names a free block).
+ */
+int pkv_seq_reorder(pkv_ba_t* ba, int32_t* tables, int32_t cap, int32_t* nblk, int32_t* seq_lens,
+                    int32_t num_rows, const int32_t* parents, int32_t* work);
 
 /* Blocks currently in the cache (in use or free). */
 int32_t pkv_ba_num_cached(const pkv_ba_t* ba);

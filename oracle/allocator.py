@@ -110,10 +110,10 @@ class BlockAllocatorModel:
         need_blocks = blocks_for_tokens(seq_len + n_new)
         if need_blocks > cap:
             raise InvalidArgument("block table too small")
-        for j in range(nblk):
-            self._check_id(int(table[j]))
-            if self.ref[int(table[j])] <= 0:
-                raise RefcountError("table holds a free block")
+        if nblk > 0:  # the one existing entry an append reads: its last block
+            self._check_id(int(table[nblk - 1]))
+            if self.ref[int(table[nblk - 1])] <= 0:
+                raise RefcountError("the last block is free")
         cow = n_new > 0 and seq_len % BLOCK_SIZE != 0 and self.ref[int(table[nblk - 1])] > 1
         if need_blocks - nblk + int(cow) > len(self.free):
             raise OutOfBlocks()
@@ -158,6 +158,36 @@ class BlockAllocatorModel:
         child = np.array(table, dtype=np.int32, copy=True)
         child[nblk:] = -1
         return child
+
+    def reorder(self, tables, nblk, seq_lens, parents):
+        """Beam reorder (blog page, beam search: candidates share their beginning): new
+        row i continues old row parents[i].  Every parent block gains one user per
+        child (child order), then every old row's blocks lose one (row order).  In
+        place on tables [R][cap], nblk [R], seq_lens [R]."""
+        R, cap = tables.shape
+        for r in range(R):
+            nb, ln, par = int(nblk[r]), int(seq_lens[r]), int(parents[r])
+            if nb < 0 or nb > cap or ln < 0 or nb != -(-ln // BLOCK_SIZE):
+                raise InvalidArgument("row lengths")
+            if not (0 <= par < R):
+                raise InvalidArgument("parent out of range")
+            for j in range(nb):
+                self._check_id(int(tables[r, j]))
+                if self.ref[int(tables[r, j])] <= 0:
+                    raise RefcountError("table holds a free block")
+        for i in range(R):
+            p = int(parents[i])
+            for j in range(int(nblk[p])):
+                self.ref[int(tables[p, j])] += 1
+        for r in range(R):
+            for j in range(int(nblk[r])):
+                self.decref(int(tables[r, j]))
+        old_t, old_n, old_l = tables.copy(), nblk.copy(), seq_lens.copy()
+        for i in range(R):
+            p = int(parents[i])
+            tables[i] = old_t[p]
+            nblk[i] = old_n[p]
+            seq_lens[i] = old_l[p]
 
     def free_seq(self, table, nblk: int):
         done = []

@@ -31,7 +31,7 @@ EXPORTS = (
     "pkv_ba_num_free", "pkv_ba_num_blocks", "pkv_blocks_for_tokens", "pkv_seq_append_slots",
     "pkv_batch_append_slots", "pkv_seq_make_writable", "pkv_seq_fork", "pkv_seq_free",
     "pkv_prefix_hash", "pkv_seq_cache_lookup", "pkv_seq_cache_seal", "pkv_ba_num_cached",
-    "pkv_ba_num_shared",
+    "pkv_ba_num_shared", "pkv_seq_reorder",
 )
 
 
@@ -98,6 +98,7 @@ def load() -> ctypes.CDLL:
         "pkv_seq_cache_seal": (ctypes.c_int, [P, pi32, i32, pi32, i32]),
         "pkv_ba_num_cached": (i32, [P]),
         "pkv_ba_num_shared": (i32, [P]),
+        "pkv_seq_reorder": (ctypes.c_int, [P, pi32, i32, pi32, pi32, i32, pi32, pi32]),
     }
     for name in EXPORTS:
         fn = getattr(lib, name)

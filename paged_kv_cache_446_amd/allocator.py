@@ -110,6 +110,15 @@ class BlockAllocator:
         _lib.check(self._lib.pkv_seq_fork(self._h, _p32(table), int(nblk), _p32(child)), "pkv_seq_fork")
         return child
 
+    def reorder(self, tables: np.ndarray, nblk: np.ndarray, seq_lens: np.ndarray, parents: np.ndarray):
+        """Beam reorder: new row i continues old row parents[i] (tables int32 [R][cap],
+        nblk/seq_lens int32 [R], updated in place)."""
+        R, cap = tables.shape
+        work = np.empty(max(R * cap, 1), dtype=np.int32)
+        par = np.ascontiguousarray(parents, dtype=np.int32)
+        _lib.check(self._lib.pkv_seq_reorder(self._h, _p32(tables), cap, _p32(nblk), _p32(seq_lens), R,
+                                             _p32(par), _p32(work)), "pkv_seq_reorder")
+
     def free_seq(self, table: np.ndarray, nblk: int):
         _lib.check(self._lib.pkv_seq_free(self._h, _p32(table), int(nblk)), "pkv_seq_free")
 

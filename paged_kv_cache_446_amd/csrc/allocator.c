@@ -246,6 +246,17 @@ int32_t pkv_ba_num_blocks(const pkv_ba_t* ba) { return ba ? ba->num_blocks : -1;
 
 /* every entry of table[0..nblk) must name an allocated block */
 static int check_table(const pkv_ba_t* ba, const int32_t* table, int32_t nblk) {
+  /* one pass without early exits (the common case: all good); on a bad entry the
+   * ordered walk below names the error of the first one */
+  if (nblk > 0 && ba->num_blocks > 0) {
+    int bad = 0;
+    for (int32_t j = 0; j < nblk; ++j) {
+      const int32_t b = table[j];
+      const int ok = (uint32_t)b < (uint32_t)ba->num_blocks;
+      bad |= !ok | (ba->ref[ok ? b : 0] <= 0);
+    }
+    if (!bad) return PKV_OK;
+  }
   for (int32_t j = 0; j < nblk; ++j) {
     if (!valid_id(ba, table[j])) return PKV_ERR_INVALID_ARGUMENT;
     if (ba->ref[table[j]] <= 0) return PKV_ERR_REFCOUNT;
@@ -265,7 +276,9 @@ int pkv_seq_append_slots(pkv_ba_t* ba, int32_t* table, int32_t cap, int32_t* nbl
   if (len + n_new > INT32_MAX) return PKV_ERR_INVALID_ARGUMENT;
   const int64_t need_blocks = pkv_blocks_for_tokens(len + n_new, PKV_BLOCK_SIZE);
   if (need_blocks > cap) return PKV_ERR_INVALID_ARGUMENT;
-  int rc = check_table(ba, table, nb);
+  /* the one existing entry this call reads (it may write into or copy that block); the
+   * rest of the table is checked by the calls that walk it (fork, reorder, free) */
+  int rc = check_table(ba, table + (nb > 0 ? nb - 1 : 0), nb > 0 ? 1 : 0);
   if (rc != PKV_OK) return rc;
   const int cow = n_new > 0 && (len % PKV_BLOCK_SIZE) != 0 && ba->ref[table[nb - 1]] > 1;
   if (need_blocks - nb + cow > ba->count) return PKV_ERR_OUT_OF_BLOCKS;
@@ -341,6 +354,73 @@ int pkv_seq_fork(pkv_ba_t* ba, const int32_t* src_table, int32_t nblk, int32_t* 
     ref_inc(ba, src_table[j]);
     dst_table[j] = src_table[j];
   }
+  return PKV_OK;
+}
+
+int pkv_seq_reorder(pkv_ba_t* ba, int32_t* tables, int32_t cap, int32_t* nblk, int32_t* seq_lens,
+                    int32_t num_rows, const int32_t* parents, int32_t* work) {
+  if (!ba || num_rows < 0 || cap < 0 || (num_rows > 0 && (!tables || !nblk || !seq_lens ||
+                                                          !parents || !work)))
+    return PKV_ERR_INVALID_ARGUMENT;
+  /* check everything first: nothing changes on an error */
+  for (int32_t r = 0; r < num_rows; ++r) {
+    if (nblk[r] < 0 || nblk[r] > cap || seq_lens[r] < 0 ||
+        nblk[r] != pkv_blocks_for_tokens(seq_lens[r], PKV_BLOCK_SIZE))
+      return PKV_ERR_INVALID_ARGUMENT;
+    if (parents[r] < 0 || parents[r] >= num_rows) return PKV_ERR_INVALID_ARGUMENT;
+    int rc = check_table(ba, tables + (int64_t)r * cap, nblk[r]);
+    if (rc != PKV_OK) return rc;
+  }
+  /* Child i and old row i often hold the same blocks in the same columns (their
+   * shared beginning): such a block gains and loses one user, stays allocated (child
+   * i keeps it) and ends with its old count, so both steps are skipped for the first
+   * same[i] columns, where the two rows agree.  What is left runs in the same order
+   * as the full walk -- gains in child order, then losses in row order -- so the
+   * final counts and the order of freed blocks are those of the full walk.  same[]
+   * lives in work until step 3 (cap >= 1 whenever a row holds a block). */
+  int32_t* same = work;
+  if (cap == 0) return PKV_OK; /* no row holds a block, every row keeps its length 0 */
+  for (int32_t i = 0; i < num_rows; ++i) {
+    const int32_t* ti = tables + (int64_t)i * cap;
+    const int32_t* tp = tables + (int64_t)parents[i] * cap;
+    const int32_t n = nblk[i] < nblk[parents[i]] ? nblk[i] : nblk[parents[i]];
+    int32_t j = 0;
+    if (parents[i] == i) j = n;
+    else
+      while (j < n && ti[j] == tp[j]) ++j;
+    same[i] = j;
+  }
+  /* every remaining gain: the counts must not overflow */
+  for (int32_t i = 0; i < num_rows; ++i) {
+    const int32_t* t = tables + (int64_t)parents[i] * cap;
+    for (int32_t j = same[i]; j < nblk[parents[i]]; ++j)
+      if (ba->ref[t[j]] > INT32_MAX - num_rows) return PKV_ERR_REFCOUNT;
+  }
+  /* 1. the children take their parents' blocks, in child order */
+  for (int32_t i = 0; i < num_rows; ++i) {
+    const int32_t* t = tables + (int64_t)parents[i] * cap;
+    for (int32_t j = same[i], n = nblk[parents[i]]; j < n; ++j) ref_inc(ba, t[j]);
+  }
+  /* 2. the old rows let go, in row order (blocks left without users join the free
+   *    queue in that order) */
+  for (int32_t r = 0; r < num_rows; ++r) {
+    const int32_t* t = tables + (int64_t)r * cap;
+    for (int32_t j = same[r], n = nblk[r]; j < n; ++j) {
+      const int32_t blk = t[j];
+      ref_dec(ba, blk);
+      if (ba->ref[blk] == 0) q_push_back(ba, blk);
+    }
+  }
+  /* 3. the new rows: copies of their parents (tables through work, then lengths) */
+  memcpy(work, tables, (size_t)num_rows * (size_t)cap * sizeof(int32_t));
+  for (int32_t i = 0; i < num_rows; ++i)
+    if (parents[i] != i)
+      memcpy(tables + (int64_t)i * cap, work + (int64_t)parents[i] * cap,
+             (size_t)cap * sizeof(int32_t));
+  for (int32_t i = 0; i < num_rows; ++i) work[i] = nblk[parents[i]];
+  for (int32_t i = 0; i < num_rows; ++i) nblk[i] = work[i];
+  for (int32_t i = 0; i < num_rows; ++i) work[i] = seq_lens[parents[i]];
+  for (int32_t i = 0; i < num_rows; ++i) seq_lens[i] = work[i];
   return PKV_OK;
 }
 

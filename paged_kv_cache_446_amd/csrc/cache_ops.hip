@@ -54,7 +54,14 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   }
 }
 
-// grid (pair, layer, K|V): copy one block of one layer of one pool.
+// grid (pair, layer, K|V): copy one block of one layer of one pool.  A block's
+// source and destination never overlap (distinct blocks), so each thread issues
+// all loads of a round before its stores: one memory round trip per kCopyBatch
+// chunks instead of one per chunk.  Loads and stores are unconditional: a lane
+// past the block's end copies its last chunk again (the same bytes to the same
+// place).
+constexpr int kCopyBatch = 8;
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restrict__ pairs,
                                                           u32x4* __restrict__ k_pool,
                                                           u32x4* __restrict__ v_pool,
@@ -64,9 +71,21 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restr
   const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
   u32x4* pool = blockIdx.z ? v_pool : k_pool;
   const int64_t base = blockIdx.y * layer_chunks;
-  const u32x4* s = pool + base + src * block_chunks;
-  u32x4* d = pool + base + dst * block_chunks;
-  for (int64_t i = threadIdx.x; i < block_chunks; i += blockDim.x) d[i] = s[i];
+  const u32x4* __restrict__ s = pool + base + src * block_chunks;
+  u32x4* __restrict__ d = pool + base + dst * block_chunks;
+  for (int64_t i0 = threadIdx.x; i0 < block_chunks; i0 += (int64_t)blockDim.x * kCopyBatch) {
+    u32x4 v[kCopyBatch];
+#pragma unroll
+    for (int k = 0; k < kCopyBatch; ++k) {  // unconditional (past the end: the last chunk)
+      const int64_t i = i0 + (int64_t)k * blockDim.x;
+      v[k] = s[i < block_chunks ? i : block_chunks - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kCopyBatch; ++k) {  // past the end: the last chunk again, same bytes
+      const int64_t i = i0 + (int64_t)k * blockDim.x;
+      d[i < block_chunks ? i : block_chunks - 1] = v[k];
+    }
+  }
 }
 
 }  // namespace pkv

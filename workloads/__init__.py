@@ -13,6 +13,7 @@ from .generate import (  # noqa: F401
     named_spec,
     scaled_spec,
     verify_spec,
+    normal_bits,
     CONFIG_NAMES,
     run_flow,
     Flow,

@@ -50,6 +50,12 @@ def _to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def normal_bits(key, shape, dtype: str) -> np.ndarray:
+    """Seeded fp32 N(0,1) values of `shape`, as raw bits of `dtype` (rng(key))."""
+    rng = np.random.default_rng(list(key))
+    return _to_bits(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
 @dataclass
 class Spec:
     """One batch: per-sequence cached context and tokens appended this step."""
