@@ -534,6 +534,38 @@ def main():
         graph_ms = ga.elapsed_time(gb) / K
         log(f"graph replay: {graph_ms * 1e3:.1f} us/step (eager {ms_step * 1e3:.1f})")
 
+    # cold cache: a 512 MiB write between reps (outside the events) evicts the
+    # 256 MB last-level cache, so attention reads its K/V from HBM
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(min(K, 20)):
+        evict.fill_(i & 255)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        attention()
+        eb.record()
+        cold.append((ea, eb))
+    torch.cuda.synchronize()
+    cold_ms = float(np.median([a.elapsed_time(b) for a, b in cold]))
+    del evict
+    # the practical read rate: one plain stream over 4 GiB (calibration kernel)
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        ops.calib_stream_read(buf, sink)
+    sr = []
+    for _ in range(10):
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        ops.calib_stream_read(buf, sink)
+        eb.record()
+        sr.append((ea, eb))
+    torch.cuda.synchronize()
+    stream_gbs = buf.numel() / (float(np.median([a.elapsed_time(b) for a, b in sr])) * 1e-3) / 1e9
+    del buf, sink
+    log(f"cold-cache attention {cold_ms * 1e3:.1f} us (warm {attn_avg * 1e3:.1f}); "
+        f"stream read {stream_gbs:.0f} GB/s")
+
     kv_bytes, attn_bytes = algorithmic_bytes(spec)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = attn_bytes / (attn_avg * 1e-3) / 1e9
@@ -583,6 +615,12 @@ def main():
             ("c3", "random", "paged") else None,
             "algorithmic_bytes_per_launch": attn_bytes,
             "avg_launch_us": round(attn_avg * 1e3, 2),
+            # a plain 4 GiB read stream on the same GPU: the practical read rate
+            "stream_read_GBps": round(stream_gbs, 1),
+            "frac_of_stream_read": round(achieved / stream_gbs, 4),
+            # the same call after a 512 MiB write evicted the last-level cache
+            "cold_cache_us": round(cold_ms * 1e3, 2),
+            "cold_cache_GBps": round(attn_bytes / (cold_ms * 1e-3) / 1e9, 2),
         },
     }
     if args.placement == "random" and alloc.num_shared() > 0:

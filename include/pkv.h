@@ -114,6 +114,18 @@ int pkv_copy_blocks(const pkv_cache_t* cache, const int32_t* pairs, int32_t num_
                     void* stream);
 
 /*
+ * Measurement only, not part of the attention path: read `bytes` of device
+ * memory at buf once, as a plain stream (16-byte non-temporal loads, several in
+ * flight per thread), on `stream`.  The time it takes is the practical HBM read
+ * rate the attention kernels are compared with, beside the nominal peak.
+ *   buf, sink  device pointers, 16-byte aligned; sink: 16 bytes the kernel may
+ *              write (a fold of the data), owned by the caller
+ *   bytes      a multiple of 16; 0 is a no-op
+ * Asynchronous; PKV_ERR_INVALID_ARGUMENT on misalignment or a NULL pointer.
+ */
+int pkv_calib_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
+
+/*
  * paged_attention: softmax attention for a batch of sequences whose K/V live
  * in the block pool.  The kernel finds every block through the block table
  * and reads K and V block by block; the result equals attention over the same

@@ -31,7 +31,7 @@ EXPORTS = (
     "pkv_ba_num_free", "pkv_ba_num_blocks", "pkv_blocks_for_tokens", "pkv_seq_append_slots",
     "pkv_batch_append_slots", "pkv_seq_make_writable", "pkv_seq_fork", "pkv_seq_free",
     "pkv_prefix_hash", "pkv_seq_cache_lookup", "pkv_seq_cache_seal", "pkv_ba_num_cached",
-    "pkv_ba_num_shared", "pkv_seq_reorder",
+    "pkv_ba_num_shared", "pkv_seq_reorder", "pkv_calib_stream_read",
 )
 
 
@@ -99,6 +99,7 @@ def load() -> ctypes.CDLL:
         "pkv_ba_num_cached": (i32, [P]),
         "pkv_ba_num_shared": (i32, [P]),
         "pkv_seq_reorder": (ctypes.c_int, [P, pi32, i32, pi32, pi32, i32, pi32, pi32]),
+        "pkv_calib_stream_read": (ctypes.c_int, [P, sz, P, P]),
     }
     for name in EXPORTS:
         fn = getattr(lib, name)

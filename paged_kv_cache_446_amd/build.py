@@ -17,7 +17,7 @@ OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(HERE, "libpkv.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["attention.hip", "prefill.hip", "cache_ops.hip", "api.cpp"]
+HIP_SOURCES = ["attention.hip", "prefill.hip", "cache_ops.hip", "calibrate.hip", "api.cpp"]
 C_SOURCES = ["allocator.c"]
 # Packed fp32 instructions stay off: ordinary float code only.
 HIP_FLAGS = [

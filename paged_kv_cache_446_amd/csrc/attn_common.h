@@ -129,7 +129,7 @@ __device__ __forceinline__ void attend_block(WaveState<DT, D>& st,
   // slots at or past the sequence end may hold anything (even NaN): select, never multiply
   const bool tail = tok0 + kBlock > n;
   if constexpr (DT::kBytes == 2) {
-    uint32_t pd0, pd1;
+    uint32_t pd0, pd1, pl0 = 0, pl1 = 0;
     if constexpr (__is_same(DT, TBF16)) {
       pd0 = pack2_bf16(p[0], p[1]);
       pd1 = pack2_bf16(p[2], p[3]);
@@ -137,11 +137,18 @@ __device__ __forceinline__ void attend_block(WaveState<DT, D>& st,
       pd0 = pack2_f16(p[0], p[1]);
       pd1 = pack2_f16(p[2], p[3]);
     }
-    // the sum uses the rounded weights, so the output is a convex combination of V rows
+    // the sum uses the weights as P.V sees them, so the output is a convex
+    // combination of V rows.  bf16 keeps 8 significant bits, too few for rows of a
+    // few keys with large values: the weights enter P.V as hi + lo, the bf16 value
+    // and its bf16 rounding residue (hi + lo is exact in fp32, about 16 bits).
     float ps;
     if constexpr (__is_same(DT, TBF16)) {
-      ps = (bf16_bits_to_f32(pd0 & 0xffffu) + bf16_bits_to_f32(pd0 >> 16)) +
-           (bf16_bits_to_f32(pd1 & 0xffffu) + bf16_bits_to_f32(pd1 >> 16));
+      const float h0 = bf16_bits_to_f32(pd0 & 0xffffu), h1 = bf16_bits_to_f32(pd0 >> 16);
+      const float h2 = bf16_bits_to_f32(pd1 & 0xffffu), h3 = bf16_bits_to_f32(pd1 >> 16);
+      pl0 = pack2_bf16(p[0] - h0, p[1] - h1);
+      pl1 = pack2_bf16(p[2] - h2, p[3] - h3);
+      ps = ((h0 + bf16_bits_to_f32(pl0 & 0xffffu)) + (h1 + bf16_bits_to_f32(pl0 >> 16))) +
+           ((h2 + bf16_bits_to_f32(pl1 & 0xffffu)) + (h3 + bf16_bits_to_f32(pl1 >> 16)));
     } else {
       ps = ((float)__builtin_bit_cast(_Float16, (uint16_t)(pd0 & 0xffffu)) +
             (float)__builtin_bit_cast(_Float16, (uint16_t)(pd0 >> 16))) +
@@ -164,6 +171,10 @@ __device__ __forceinline__ void attend_block(WaveState<DT, D>& st,
     for (int i = 0; i < Gm::kChunks; ++i) {
       st.acc[2 * i] = mma_k16(vr[i].x, vr[i].y, pd0, pd1, st.acc[2 * i], DT());
       st.acc[2 * i + 1] = mma_k16(vr[i].z, vr[i].w, pd0, pd1, st.acc[2 * i + 1], DT());
+      if constexpr (__is_same(DT, TBF16)) {
+        st.acc[2 * i] = mma_k16(vr[i].x, vr[i].y, pl0, pl1, st.acc[2 * i], DT());
+        st.acc[2 * i + 1] = mma_k16(vr[i].z, vr[i].w, pl0, pl1, st.acc[2 * i + 1], DT());
+      }
     }
   } else {
     st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));

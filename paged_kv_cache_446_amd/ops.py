@@ -105,3 +105,12 @@ def contiguous_attention(cache: PagedCache, out, q, first_block, seq_lens, query
                                             S, Tq, max_seq_len, num_q_heads, float(scale),
                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _stream(stream)), "pkv_contiguous_attention")
+
+
+def calib_stream_read(buf, sink, stream=None):
+    """Measurement only: read all of `buf` (a device tensor, size a multiple of 16
+    bytes) once as a plain stream; `sink` is a 16-byte device tensor it may write."""
+    lib = _lib.load()
+    assert buf.is_contiguous() and sink.numel() * sink.element_size() >= 16
+    _lib.check(lib.pkv_calib_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                         _stream(stream)), "pkv_calib_stream_read")

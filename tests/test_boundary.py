@@ -62,6 +62,12 @@ def test_host_side_argument_checks_without_gpu():
     assert lib.pkv_paged_attention(ctypes.byref(ok), 0, 16, 16, 16, 8, 16, 16, 1, 1, 1, 16, 32,
                                    0.1, 16, 1 << 20, 2, None) == -1
     assert lib.pkv_paged_attention_workspace_bytes(256, 256, 8192, 32, 128) > 0
+    # the stream-read calibration checks its arguments before launching anything
+    assert lib.pkv_calib_stream_read(None, 0, None, None) == 0  # nothing to read
+    assert lib.pkv_calib_stream_read(None, 64, 16, None) == -1
+    assert lib.pkv_calib_stream_read(16, 64, None, None) == -1
+    assert lib.pkv_calib_stream_read(24, 64, 16, None) == -1  # misaligned buffer
+    assert lib.pkv_calib_stream_read(16, 60, 16, None) == -1  # not whole 16-byte units
 
 
 def _random_ops(seed, alloc, n_ops=400):

@@ -67,6 +67,16 @@ def test_group_sizes_and_head_dims(dtype, hq, hkv, d):
     _check(spec, f"{dtype} {hq}/{hkv} d{d}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_chunks_over_empty_context(dtype):
+    # first chunks of prompts: row i sees only i + 1 keys, so early rows have outputs
+    # of the size of single V rows (the largest errors a 16-bit path makes)
+    ctx = np.array([0, 0, 0, 3], dtype=np.int64)
+    q = np.array([64, 200, 17, 90], dtype=np.int64)
+    spec = workloads.make_spec(f"empty-ctx-{dtype}", (446, 99, len(dtype)), dtype, 32, 8, 128, ctx, q)
+    _check(spec, f"chunks over an empty context {dtype}")
+
+
 def test_chunks_over_long_context():
     # a chunk over a 32768-token context (the mixed batch's upper bound) and a decode
     ctx = np.array([32768, 8191, 100], dtype=np.int64)
@@ -297,6 +307,40 @@ def test_shared_prefix_hint_changes_no_bits(name, kw):
     assert np.array_equal(plain, run.out_bits())
     if name == "c4":
         assert run.alloc.num_shared() > 0
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 8, 1, 64), ("f32", 8, 8, 64),
+                                            ("bf16", 16, 2, 256), ("f16", 16, 8, 128)])
+def test_shared_prefix_order_changes_no_bits_across_shapes(dtype, hq, hkv, d):
+    # The shared-prefix order lists partitions partition-major and deals units
+    # head-major; sequence order lists them row by row.  Both run the same
+    # per-partition arithmetic and the same merge.
+    import torch
+
+    gp = _gp()
+    n = np.array([1, 1023, 1024, 1025, 2049, 3073, 64, 17, 2048, 5], dtype=np.int64)
+    spec = workloads.make_spec(f"orders-{dtype}", (446, 98, hq, hkv, d), dtype, hq, hkv, d, n - 1,
+                               np.ones_like(n))
+    run = gp.prepare(spec, run_attention=False)
+    gp.attention(run, shared_prefixes=False)
+    torch.cuda.synchronize()
+    plain = run.out_bits().copy()
+    gp.attention(run, shared_prefixes=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(plain, run.out_bits())
+
+
+@pytest.mark.parametrize("rows", [257, 1024, 1025])
+def test_decode_row_counts_around_the_plan_thread_limit(rows):
+    # The plan kernel's 1024 threads hold one row each up to 1024 rows, two past
+    # that.  Short rows plus a few that span several 1024-token partitions.  The
+    # rows of a few tokens give outputs up to |o| ~ 3.6, where bf16 keeps only
+    # 2^-7 relative: the weights must enter P.V with more than bf16's 8 bits.
+    rng = np.random.default_rng([446, 97, rows])
+    n = rng.integers(1, 40, size=rows, endpoint=True)
+    n[rng.choice(rows, size=5, replace=False)] = [1025, 2048, 2049, 3000, 1500]
+    spec = workloads.make_spec(f"rows{rows}", (446, 97, rows), "bf16", 8, 2, 64, n - 1, np.ones_like(n))
+    _check(spec, f"{rows} rows")
 
 
 def _contiguous_pool(spec, gp):
