@@ -46,7 +46,12 @@ def _run(cmd):
 
 # Per-source extra flags.  prefill.hip: its maxima never see a NaN (stale slots are
 # removed by selection first), so the compiler may drop NaN-quieting before each max.
-EXTRA_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
+# The plan kernels add per-thread counts into shared counters: an atomic add whose
+# address is the same for the whole wavefront is combined across the wavefront with
+# DPP row operations, not with a scalar loop over the active lanes (one readlane and
+# one LDS wait per lane).
+ATOMIC_DPP = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=DPP"]
+EXTRA_FLAGS = {"prefill.hip": ["-fno-honor-nans"] + ATOMIC_DPP, "attention.hip": ATOMIC_DPP}
 
 
 def build(verbose: bool = False) -> str:

@@ -26,9 +26,10 @@
 // its four wavefronts take every fourth block, streaming K/V tiles with
 // non-temporal loads (each tile is read once), merge through LDS, and a
 // second kernel merges the partitions of long sequences with the log-sum-exp
-// rule.  Workgroup ids are remapped so that the eight KV heads of one
-// partition, and neighbouring partitions, run on the same XCD (hardware
-// dispatch deals consecutive workgroups round-robin over the eight XCDs).
+// rule.  Work items are listed longest first and workgroup ids are remapped
+// so that every XCD takes its share of them in that order, with the KV heads
+// of one item together on one XCD (hardware dispatch deals consecutive
+// workgroups round-robin over the eight XCDs).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -37,7 +38,10 @@
 
 namespace pkv {
 
-constexpr int kPartBlocks = 64;  // blocks per decode partition (1024 tokens)
+constexpr int kPartBlocks = 64;  // blocks of the shortest decode partition (1024 tokens)
+constexpr int kPartChoices = 4;  // partitions of 1, 2, 3 or 4 x kPartBlocks blocks
+constexpr int kPartMax = kPartChoices * kPartBlocks;
+constexpr int kGpuCUs = 256;     // compute units of an MI355X
 constexpr int kPlanLevels = 2048;  // partition indices the plan orders items by (2M tokens)
 
 // ---------------------------------------------------------------------------
@@ -68,17 +72,21 @@ struct alignas(16) DecodeItem {
 };
 
 // Work lists of one call, written by decode_plan_kernel: the items of one-tile
-// rows (class 1) and of two-tile rows (class 2), with h = 0, in sequence order,
-// or partition-major when the caller says that rows share prefixes of blocks
-// (PKV_ATTN_SHARED_PREFIXES): partition 0 of every row, then partition 1 of
-// every row that has one, and so on (sequence order within a partition index is
-// not kept).  Rows that share blocks then read them at about the same time, on
-// the same XCD, so its L2 serves most of those reads; without sharing, sequence
-// order spreads long and short rows evenly over the XCDs.  Workgroup units are
-// (item, KV head) pairs, item-major, dealt to the eight XCDs in contiguous runs
-// (xcd_unit).  Sequences split over several partitions own workspace rows from
-// base[s]: row base[s] + (p * q_len + t) * Hq + head holds partition p's result
-// for query token t; one merge entry per (split sequence, query token).
+// rows (class 1) and of two-tile rows (class 2), with h = 0, longest first
+// (blocks per item, descending), or partition-major when the caller says that
+// rows share prefixes of blocks (PKV_ATTN_SHARED_PREFIXES): partition 0 of every
+// row, then partition 1 of every row that has one, and so on.  The order within
+// one length or partition index is not kept.
+//   Longest first: the items are dealt to the eight XCDs in rounds of eight, in
+//   alternating directions, with the KV heads of an item together, so every XCD
+//   takes its share of the long items first and the short ones fill the gaps at
+//   the end (list scheduling, longest processing time first).
+//   Partition-major: rows that share blocks read them at about the same time, so
+//   an XCD's L2 serves most of those reads; workgroup units are (KV head, item)
+//   pairs dealt to the eight XCDs in contiguous runs (xcd_unit).
+// A sequence split over several partitions owns a run of workspace rows from some
+// base r: row r + (p * q_len + t) * Hq + head holds partition p's result for query
+// token t; one merge entry per (split sequence, query token).
 // One merge: the output query row, the partition count, the workspace row of
 // (partition 0, this token, head 0) and the rows between partitions.
 struct MergeEntry {
@@ -91,17 +99,17 @@ struct DecodePlan {
                       // nullptr: no plan, every row is one item (single-partition batches)
   DecodeItem* items;  // [2][cap]
   MergeEntry* merge;  // [num_seqs * 32]
-  int64_t* base;      // [num_seqs]
   int num_seqs;
   int cap;            // num_seqs * max_parts
-  int head_major;     // units ordered (KV head, item) instead of (item, KV head)
+  int by_part;        // partition-major lists, units (KV head, item) in XCD runs;
+                      // otherwise longest first, dealt to the XCDs in rounds of 8 items
 };
 
-// Blocks per partition of a row: 1024 tokens for decode rows; a multi-token row
-// uses 1024 << shift, with the shift the plan chose so that the split rows fit
-// the workspace.
-__device__ __forceinline__ int part_blocks(int q_len, int shift) {
-  return q_len > 1 ? kPartBlocks << shift : kPartBlocks;
+// Blocks per partition of a row: pb for decode rows, the size the plan chose for
+// the call; a multi-token row uses pb << shift, with the shift the plan chose so
+// that the split rows fit the workspace.
+__device__ __forceinline__ int part_blocks(int q_len, int pb, int shift) {
+  return q_len > 1 ? pb << shift : pb;
 }
 
 // Column-tile class of a row: 1 or 2, or 0 for rows left to the prefill kernels
@@ -112,22 +120,61 @@ __device__ __forceinline__ int row_class(int q_len, int max_q, int G, int max_co
   return cols <= 16 ? 1 : 2;
 }
 
+// Fixed cost of one decode workgroup (launch, metadata, Q, merge through LDS) in
+// the plan's time unit, one 16-token block step of a wavefront.
+constexpr int kUnitCost = 2;
+// An HBM write of split partials among the K/V reads costs about as much time as
+// reading this many times its bytes (measured on the GQA decode workload).
+constexpr int kPartialWeight = 11;
+// Length bins of decode items: ceil(blocks / 4) - 1, the block steps of each wavefront
+// of the workgroup minus one (items of the longest partition in the last bin).
+constexpr int kSizeBins = kPartMax / kWaves;
+static_assert(kSizeBins == kWave, "one length bin per lane");
+
+__device__ __forceinline__ int size_bin(int blocks) {
+  return blocks > 0 ? min((blocks + kWaves - 1) / kWaves, kSizeBins) - 1 : 0;
+}
+
 // One workgroup of 1024 threads; thread t owns sequences [t*k, t*k + k).  A
 // small row of a sequence with n > 0 tokens has one item per partition; an
 // empty sequence has one item (its zero output).  A split row has one merge
 // entry per query token.  budget: workspace rows for split rows
-// (each row is head_dim floats).  The partition shift starts at 0 and grows
-// until the split rows fit; this terminates, since once a partition spans
-// max_parts * 1024 tokens no multi-token row is split, and decode rows alone
-// need at most num_seqs * max_parts * hq rows.
+// (each row is head_dim floats).
+//
+// Partition size.  The decode workgroups are list-scheduled, longest first, onto
+// `slots` resident workgroups.  For each size of 1 to kPartChoices times
+// kPartBlocks blocks the plan estimates the finish time in block steps: the ideal
+// sum over (item, KV head) units of kUnitCost + ceil(blocks / 4) divided by
+// slots; at least j + 1 times the (j * slots + 1)-th longest unit for j >= 0,
+// since some workgroup runs j + 1 of the j * slots + 1 longest; plus the split
+// partials' bytes weighed as kPartialWeight times K/V bytes.  The smallest
+// estimate wins (ties: the larger partition, fewer partials).  Rows that share
+// blocks (PKV_ATTN_SHARED_PREFIXES) keep kPartBlocks: their reads come mostly
+// from L2, and more, shorter partitions read together serve more of them from
+// there.  The partition size sets the rounding order of a row's sums, so it is
+// the one way the batch and the hint reach a row's output bits (within the
+// tolerance of the arithmetic: the result is the same attention).
+//
+// The partition shift of multi-token rows starts at 0 and grows until the split
+// rows fit; this terminates, since once a partition spans max_parts * 1024
+// tokens no multi-token row is split, and decode rows alone need at most
+// num_seqs * max_parts * hq rows.
+//
+// Lists are counting-sorted by key: the length bin, longest first (the same
+// per-bin counts the estimate used, while no multi-token row changed its
+// partition size), or the partition index (partition-major).  Merge entries and
+// workspace rows are handed out by atomic counters, in no particular order.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int num_seqs,
     int bt_stride, int max_parts, int max_q, int G, int max_cols, int hq, long long budget,
-    int order_by_part, DecodePlan plan) {
-  __shared__ int sm_tot[3][1024 / kWave];
-  __shared__ long long sm_rows[1024 / kWave];
-  __shared__ int sm_lvl[2][kPlanLevels];  // items per partition index, then cursors
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nwaves = blockDim.x / kWave;
+    int num_kv_heads, int slots, int row_bytes, int step_bytes, DecodePlan plan) {
+  __shared__ int sm_hist[2][kPartChoices][kSizeBins];     // items per class, size, length bin
+  __shared__ unsigned long long sm_pbytes[kPartChoices];  // split partials' bytes, per size
+  __shared__ float sm_est[kPartChoices];
+  __shared__ int sm_lvl[2][kPlanLevels];  // items per list key and class, then cursors
+  __shared__ int sm_cnt[4];               // class-1 items, class-2 items, merge entries, cursor
+  __shared__ unsigned long long sm_rows[2];  // workspace rows of split rows; cursor
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int k = (num_seqs + blockDim.x - 1) / blockDim.x;
   const int s0 = tid * k;
   auto blocks = [&](int n) {
@@ -143,123 +190,193 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
   auto qb_of = [&](int s) { return k == 1 ? c_qb : qsl[s]; };
   auto qlen_of = [&](int s) { return k == 1 ? c_qe - c_qb : qsl[s + 1] - qsl[s]; };
   auto n_of = [&](int s) { return k == 1 ? c_n : seq_lens[s]; };
-  const int levels = max_parts < kPlanLevels ? max_parts : kPlanLevels;
-  for (int i = tid; i < 2 * levels; i += blockDim.x) sm_lvl[i / levels][i % levels] = 0;
-  int shift = 0, n1, n2, nmg, x1, x2, xm;
-  long long nrow, xr, trow;
-  for (;; ++shift) {
-    n1 = n2 = nmg = 0;
-    nrow = 0;
+  const bool by_part = plan.by_part;
+  const bool choose = max_parts > 1 && !by_part;
+  for (int i = tid; i < 2 * kPartChoices * kSizeBins; i += blockDim.x) (&sm_hist[0][0][0])[i] = 0;
+  if (by_part)
+    for (int i = tid; i < 2 * max_parts; i += blockDim.x) sm_lvl[i / max_parts][i % max_parts] = 0;
+  if (tid < kPartChoices) sm_pbytes[tid] = 0;
+  if (tid < 4) sm_cnt[tid] = 0;
+  if (tid < 2) sm_rows[tid] = 0;
+  __syncthreads();
+
+  // 1. items per class, partition size and length bin; split partials' bytes per size
+  if (choose) {
+    unsigned long long pbytes[kPartChoices] = {};
     for (int j = 0; j < k; ++j) {
       const int s = s0 + j;
       if (s >= num_seqs) break;
       const int q_len = qlen_of(s);
       const int cls = row_class(q_len, max_q, G, max_cols);
       if (!cls) continue;
-      const int n = n_of(s), pb = part_blocks(q_len, shift);
+      const int nb = blocks(n_of(s));
+#pragma unroll
+      for (int c = 0; c < kPartChoices; ++c) {
+        const int pb = (c + 1) * kPartBlocks, f = nb / pb, rem = nb - f * pb;
+        if (f) atomicAdd(&sm_hist[cls - 1][c][size_bin(pb)], f);
+        if (rem || !nb) atomicAdd(&sm_hist[cls - 1][c][size_bin(rem)], 1);
+        if (f + (rem > 0) > 1) pbytes[c] += (unsigned long long)(f + (rem > 0)) * q_len * hq * row_bytes;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kPartChoices; ++c)
+      if (pbytes[c]) atomicAdd(&sm_pbytes[c], pbytes[c]);
+  }
+  __syncthreads();
+
+  // 2. the estimate of each size: wavefront c for size c, lane i for length bin i
+  if (choose) {
+    if (w < kPartChoices) {
+      const long long cnt = (long long)(sm_hist[0][w][lane] + sm_hist[1][w][lane]) * num_kv_heads;
+      const int t = kUnitCost + lane + 1;
+      long long work = cnt * t;  // summed over the wavefront below
+      long long suf = cnt;       // inclusive suffix sum: units in this bin and longer ones
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const long long y = __shfl_down(suf, off);
+        if (lane + off < kWave) suf += y;
+      }
+      const long long above = suf - cnt;  // units in longer bins
+      float bound = 0.f;
+      if (cnt > 0) {
+        const long long jhi = (suf - 1) / slots;  // largest j with j * slots + 1 <= suf
+        if (jhi * slots >= above) bound = (float)((jhi + 1) * t);
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        work += __shfl_xor(work, off);
+        bound = fmaxf(bound, __shfl_xor(bound, off));
+      }
+      const float est = fmaxf(bound, (float)work / slots +
+                                         (float)sm_pbytes[w] * kPartialWeight / ((float)step_bytes * slots));
+      if (lane == 0) sm_est[w] = est;
+    }
+  } else if (tid < kPartChoices) {
+    // one partition spans every row, or rows share blocks: kPartBlocks
+    sm_est[tid] = tid ? INFINITY : 0.f;
+  }
+  __syncthreads();
+  int pb0 = kPartBlocks;  // the smallest estimate; ties: the larger partition
+  {
+    float e = sm_est[0];
+#pragma unroll
+    for (int c = 1; c < kPartChoices; ++c)
+      if (sm_est[c] <= e) {
+        e = sm_est[c];
+        pb0 = (c + 1) * kPartBlocks;
+      }
+  }
+
+  // 3. totals: items of each class, merge entries, workspace rows (and the shift)
+  int shift = 0;
+  for (;; ++shift) {
+    int n1 = 0, n2 = 0, nmg = 0;
+    unsigned long long nrow = 0;
+    for (int j = 0; j < k; ++j) {
+      const int s = s0 + j;
+      if (s >= num_seqs) break;
+      const int q_len = qlen_of(s);
+      const int cls = row_class(q_len, max_q, G, max_cols);
+      if (!cls) continue;
+      const int n = n_of(s), pb = part_blocks(q_len, pb0, shift);
       const int np = n > 0 ? (blocks(n) + pb - 1) / pb : 1;
       (cls == 1 ? n1 : n2) += np;
       if (np > 1) {
         nmg += q_len;
-        nrow += (long long)np * q_len * hq;
+        nrow += (unsigned long long)np * q_len * hq;
       }
     }
-    // inclusive prefix of (n1, n2, nmg, nrow) within the wavefront, then wave totals
-    x1 = n1, x2 = n2, xm = nmg, xr = nrow;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y1 = __shfl_up(x1, off), y2 = __shfl_up(x2, off), ym = __shfl_up(xm, off);
-      const long long yr = __shfl_up(xr, off);
-      if (lane >= off) {
-        x1 += y1;
-        x2 += y2;
-        xm += ym;
-        xr += yr;
-      }
-    }
-    if (lane == kWave - 1) {
-      sm_tot[0][w] = x1;
-      sm_tot[1][w] = x2;
-      sm_tot[2][w] = xm;
-      sm_rows[w] = xr;
-    }
+    if (n1) atomicAdd(&sm_cnt[0], n1);
+    if (n2) atomicAdd(&sm_cnt[1], n2);
+    if (nmg) atomicAdd(&sm_cnt[2], nmg);
+    if (nrow) atomicAdd(&sm_rows[0], nrow);
     __syncthreads();
-    trow = 0;
-    for (int ww = 0; ww < nwaves; ++ww) trow += sm_rows[ww];
-    if (trow <= budget || (kPartBlocks << shift) >= max_parts * kPartBlocks) break;
-    __syncthreads();  // every wave has read the totals before the next round writes them
+    if ((long long)sm_rows[0] <= budget || (pb0 << shift) >= max_parts * kPartBlocks) break;
+    __syncthreads();  // every thread has read the total before it is cleared
+    if (tid < 3) sm_cnt[tid] = 0;
+    if (tid == 0) sm_rows[0] = 0;
+    __syncthreads();
   }
-  int b1 = 0, b2 = 0, bm = 0, t1 = 0, t2 = 0, tm = 0;
-  long long br = 0;
-  for (int ww = 0; ww < nwaves; ++ww) {
-    if (ww < w) {
-      b1 += sm_tot[0][ww];
-      b2 += sm_tot[1][ww];
-      bm += sm_tot[2][ww];
-      br += sm_rows[ww];
-    }
-    t1 += sm_tot[0][ww];
-    t2 += sm_tot[1][ww];
-    tm += sm_tot[2][ww];
-  }
-  int p1 = b1 + x1 - n1, p2 = b2 + x2 - n2, pm = bm + xm - nmg;
-  long long pr = br + xr - nrow;
-  // partition-major lists: items per partition index, their starts, then cursors
-  const bool by_part = order_by_part && max_parts <= kPlanLevels;
-  if (by_part) {
+
+  // 4. list keys and their starts.  Longest first with unchanged partition sizes: the
+  //    counts of step 1 (one key per lane); otherwise counted here
+  const bool from_hist = choose && shift == 0;
+  const int ci = pb0 / kPartBlocks - 1;
+  const int levels = by_part ? max_parts : kSizeBins;
+  auto key = [&](int p, int nb, int pb) {
+    return by_part ? p : kSizeBins - 1 - size_bin(min(nb, (p + 1) * pb) - p * pb);
+  };
+  if (!from_hist) {
+    if (!by_part)
+      for (int i = tid; i < 2 * kSizeBins; i += blockDim.x) sm_lvl[i / kSizeBins][i % kSizeBins] = 0;
+    __syncthreads();
     for (int j = 0; j < k; ++j) {
       const int s = s0 + j;
       if (s >= num_seqs) break;
       const int q_len = qlen_of(s);
       const int cls = row_class(q_len, max_q, G, max_cols);
       if (!cls) continue;
-      const int n = n_of(s), pb = part_blocks(q_len, shift);
-      const int np = n > 0 ? (blocks(n) + pb - 1) / pb : 1;
-      for (int p = 0; p < np; ++p) atomicAdd(&sm_lvl[cls - 1][p], 1);
-    }
-    __syncthreads();
-    if (tid < 2) {  // exclusive scan over the partition indices of one class
-      int run = 0;
-      for (int p = 0; p < max_parts; ++p) {
-        const int c = sm_lvl[tid][p];
-        sm_lvl[tid][p] = run;
-        run += c;
-      }
+      const int n = n_of(s), nb = blocks(n), pb = part_blocks(q_len, pb0, shift);
+      const int np = n > 0 ? (nb + pb - 1) / pb : 1;
+      for (int p = 0; p < np; ++p) atomicAdd(&sm_lvl[cls - 1][key(p, nb, pb)], 1);
     }
     __syncthreads();
   }
+  if (w < 2) {  // exclusive scan over the keys of class w + 1: lane i owns a run of keys
+    const int per = (levels + kWave - 1) / kWave;
+    const int v0 = min(lane * per, levels), v1 = min(v0 + per, levels);
+    int sum = 0;
+    if (from_hist)
+      sum = sm_hist[w][ci][kSizeBins - 1 - lane];
+    else
+      for (int v = v0; v < v1; ++v) sum += sm_lvl[w][v];
+    int x = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    int run = x - sum;
+    if (from_hist) {
+      sm_lvl[w][lane] = run;
+    } else {
+      for (int v = v0; v < v1; ++v) {
+        const int c = sm_lvl[w][v];
+        sm_lvl[w][v] = run;
+        run += c;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 5. items at their keys' cursors; merge entries and workspace rows of split rows
   for (int j = 0; j < k; ++j) {
     const int s = s0 + j;
     if (s >= num_seqs) break;
     const int q_len = qlen_of(s);
     const int cls = row_class(q_len, max_q, G, max_cols);
     if (!cls) continue;
-    const int n = n_of(s), nb = blocks(n), pb = part_blocks(q_len, shift);
+    const int n = n_of(s), nb = blocks(n), pb = part_blocks(q_len, pb0, shift);
     const int np = n > 0 ? (nb + pb - 1) / pb : 1;
     const int qb = qb_of(s);
-    DecodeItem* rec = plan.items + (cls == 1 ? (int64_t)p1 : (int64_t)plan.cap + p2);
-    DecodeItem* list = plan.items + (cls == 1 ? 0 : (int64_t)plan.cap);
-    for (int p = 0; p < np; ++p) {
-      const DecodeItem d{s, 0, p * pb, min(nb, (p + 1) * pb), qb, q_len, n, p,
-                         np > 1 ? pr + (long long)p * q_len * hq : -1, 0};
-      if (by_part)
-        list[atomicAdd(&sm_lvl[cls - 1][p], 1)] = d;
-      else
-        rec[p] = d;
-    }
-    (cls == 1 ? p1 : p2) += np;
+    long long pr = -1;
     if (np > 1) {
+      pr = (long long)atomicAdd(&sm_rows[1], (unsigned long long)np * q_len * hq);
+      const int pm = atomicAdd(&sm_cnt[3], q_len);
       for (int t = 0; t < q_len; ++t)
-        plan.merge[pm++] =
+        plan.merge[pm + t] =
             MergeEntry{qb + t, np, 0, 0, pr + (long long)t * hq, (long long)q_len * hq};
-      plan.base[s] = pr;
-      pr += (long long)np * q_len * hq;
     }
+    DecodeItem* list = plan.items + (cls == 1 ? 0 : (int64_t)plan.cap);
+    for (int p = 0; p < np; ++p)
+      list[atomicAdd(&sm_lvl[cls - 1][key(p, nb, pb)], 1)] =
+          DecodeItem{s, 0, p * pb, min(nb, (p + 1) * pb), qb, q_len, n, p,
+                     np > 1 ? pr + (long long)p * q_len * hq : -1, 0};
   }
   if (tid == 0) {
-    plan.counts[0] = t1;
-    plan.counts[1] = tm;
-    plan.counts[2] = t2;
+    plan.counts[0] = sm_cnt[0];
+    plan.counts[1] = sm_cnt[2];
+    plan.counts[2] = sm_cnt[1];
   }
 }
 
@@ -279,15 +396,28 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
   DecodeItem it;
   if (plan.counts) {
     const int live = plan.counts[CT == 1 ? 0 : 2];
-    const int j = xcd_unit(blockIdx.x, live * num_kv_heads);
-    if (j < 0) return;
-    // units item-major (the KV heads of an item together), or head-major for rows that
-    // share blocks (the rows reading one (block, head) tile run together)
-    const int i = plan.head_major ? j % live : j / num_kv_heads;
+    int i, h;
+    if (plan.by_part) {
+      // head-major units in XCD runs: the rows reading one (block, head) tile run together
+      const int j = xcd_unit(blockIdx.x, live * num_kv_heads);
+      if (j < 0) return;
+      i = j % live;
+      h = j / live;
+    } else {
+      // longest first: the r-th workgroup of XCD x takes KV head r % H of the item at
+      // position x of round r / H of the list, counted from the other end in odd rounds
+      // (so no XCD takes the longest item of every round).  Past the list, and so last
+      // on every XCD, it returns.
+      const int x = blockIdx.x % kXcds, r = blockIdx.x / kXcds;
+      const int rd = r / num_kv_heads;
+      i = rd * kXcds + ((rd & 1) ? kXcds - 1 - x : x);
+      h = r % num_kv_heads;
+      if (i >= live) return;
+    }
     it = plan.items[(CT == 1 ? 0 : (int64_t)plan.cap) + i];
     asm volatile("" : "+s"(it.s), "+s"(it.b0), "+s"(it.b1), "+s"(it.qb), "+s"(it.q_len),
                  "+s"(it.n), "+s"(it.part), "+s"(it.wrow));
-    it.h = plan.head_major ? j / live : j % num_kv_heads;
+    it.h = h;
     if (it.wrow >= 0) it.wrow += it.h * G;
   } else {  // one partition per row: every sequence is an item
     const int j = xcd_unit(blockIdx.x, plan.num_seqs * num_kv_heads);
@@ -488,13 +618,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 // counts, the item records of two classes, merge entries (up to 32 query tokens per
-// sequence), row bases
+// sequence)
 static int64_t plan_item_bytes(int64_t num_seqs, int64_t max_parts) {
   return round256(256 + 2 * num_seqs * max_parts * (int64_t)sizeof(DecodeItem));
 }
 static int64_t decode_plan_bytes(int64_t num_seqs, int64_t max_parts) {
-  return plan_item_bytes(num_seqs, max_parts) +
-         round256(num_seqs * 32 * (int64_t)sizeof(MergeEntry)) + round256(num_seqs * 8);
+  return plan_item_bytes(num_seqs, max_parts) + round256(num_seqs * 32 * (int64_t)sizeof(MergeEntry));
 }
 
 // Workspace rows (head_dim floats each) for the partial results of split rows:
@@ -507,9 +636,12 @@ static int64_t split_rows(int64_t num_seqs, int64_t max_parts, int64_t num_q_hea
 template <class DT, int D, int G, int CT>
 static int launch_ct(const AttnArgs& a, const DecodePlan& plan) {
   typedef typename DT::T T;
-  // grids sized for every sequence in every partition; the plan's counts cut them short
-  const int64_t units = (int64_t)a.num_kv_heads * a.max_parts * a.num_seqs;
-  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds;
+  // grids sized for every sequence in every partition (whole rounds of 8 items for the
+  // longest-first mapping); the plan's counts cut them short
+  const int64_t items = (int64_t)a.max_parts * a.num_seqs;
+  const int64_t grid = plan.counts && !plan.by_part
+                           ? (items + kXcds - 1) / kXcds * kXcds * a.num_kv_heads
+                           : (items * a.num_kv_heads + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((decode_kernel<DT, D, G, CT>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                      (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
                      a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, a.max_parts, a.max_q_len,
@@ -524,28 +656,32 @@ static int launch(const AttnArgs& a) {
   DecodePlan plan;
   plan.num_seqs = a.num_seqs;
   plan.cap = a.num_seqs * a.max_parts;
-  plan.head_major = a.order_by_part ? 1 : 0;
+  // partition-major needs one list key per partition index
+  plan.by_part = a.order_by_part && a.max_parts <= kPlanLevels ? 1 : 0;
   plan.counts = nullptr;
   plan.items = nullptr;
   plan.merge = nullptr;
-  plan.base = nullptr;
+  // a class no row can be in is not launched: two-tile rows need max_q_len * G > 16,
+  // and rows of one q_len are all in the same class
+  const int64_t widest = (int64_t)a.max_q_len * G;
+  const bool two_only = a.uniform_q && widest > 16;
+  // resident decode workgroups the plan balances over: those of the one-tile kernel,
+  // unless every row takes two tiles
+  const int slots = kGpuCUs * (two_only ? decode_occupancy<DT, D, 2>() : decode_occupancy<DT, D, 1>());
   if (a.max_parts > 1) {
     // sequences may span several partitions: list the live (sequence, partition) items
     plan.counts = (int32_t*)a.ws_plan;
     plan.items = (DecodeItem*)((char*)a.ws_plan + 256);
     char* mp = (char*)a.ws_plan + plan_item_bytes(a.num_seqs, a.max_parts);
     plan.merge = (MergeEntry*)mp;
-    plan.base = (int64_t*)(mp + round256((int64_t)a.num_seqs * 32 * sizeof(MergeEntry)));
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
                        a.num_seqs, a.bt_stride, a.max_parts, a.max_q_len, G, kMaxCols,
                        a.num_kv_heads * G,
                        (long long)split_rows(a.num_seqs, a.max_parts, a.num_kv_heads * G),
-                       a.order_by_part ? 1 : 0, plan);
+                       a.num_kv_heads, slots,
+                       (D + 2) * 4, kWaves * 2 * kBlock * D * DT::kBytes, plan);
   }
-  // a class no row can be in is not launched: two-tile rows need max_q_len * G > 16,
-  // and rows of one q_len are all in the same class
-  const int64_t widest = (int64_t)a.max_q_len * G;
-  if (!(a.uniform_q && widest > 16) && launch_ct<DT, D, G, 1>(a, plan) != PKV_OK) return PKV_ERR_HIP;
+  if (!two_only && launch_ct<DT, D, G, 1>(a, plan) != PKV_OK) return PKV_ERR_HIP;
   if constexpr (kMaxCols > 16)
     if (widest > 16 && launch_ct<DT, D, G, 2>(a, plan) != PKV_OK) return PKV_ERR_HIP;
   if (a.max_parts > 1) {
@@ -631,7 +767,7 @@ static int attention_impl(const pkv_cache_t* cache, int32_t layer, void* out, co
   if (cache->dtype == PKV_F32 && cache->head_dim == 256) return PKV_ERR_UNSUPPORTED;
   // the decode and merge grids (padded to whole XCD rounds) must fit their limit
   const int64_t per_seq = max_partitions(max_seq_len) > 32 ? max_partitions(max_seq_len) : 32;
-  if ((int64_t)num_seqs * cache->num_kv_heads * per_seq + kXcds > 0x7fffffff)
+  if (((int64_t)num_seqs * per_seq + kXcds) * cache->num_kv_heads > 0x7fffffff)
     return PKV_ERR_INVALID_ARGUMENT;
   const size_t need = pkv_paged_attention_workspace_bytes(num_seqs, num_q_tokens, max_seq_len,
                                                           num_q_heads, cache->head_dim);

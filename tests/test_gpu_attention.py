@@ -293,7 +293,8 @@ def test_prefill_split_deterministic_and_placement_invariant():
     ("c5", dict(num_seqs=12, max_len=1500, variant=6)),
 ])
 def test_shared_prefix_hint_changes_no_bits(name, kw):
-    # the hint only reorders the work (rows that share blocks read them together)
+    # batches whose plan keeps 1024-token partitions either way: the hint only
+    # reorders the work (rows that share blocks read them together)
     import torch
 
     gp = _gp()

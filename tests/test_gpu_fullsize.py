@@ -75,3 +75,44 @@ def _v_ranges(spec):
         vf = numerics.to_f64(v, spec.dtype)
         lo[s], hi[s] = vf.min(axis=0), vf.max(axis=0)
     return lo, hi
+
+
+def _partition_batch(kind):
+    """Decode batches (1 KV head, 4 query heads, head_dim 64, bf16) large enough that the
+    plan's estimate picks decode partitions of 2048, 3072 or 4096 tokens (small batches
+    keep 1024), with lengths planted on both sides of one and two partitions."""
+    if kind == 2048:
+        n = np.full(256, 6000, dtype=np.int64)
+        n[:6] = [2047, 2048, 2049, 4095, 4096, 4097]
+    elif kind == 3072:
+        n = np.full(512, 4096, dtype=np.int64)
+        n[:6] = [3071, 3072, 3073, 6143, 6144, 6145]
+    else:
+        rng = np.random.default_rng([446, 102])
+        n = np.clip(np.rint(np.exp(rng.uniform(np.log(64), np.log(16384), 1024))), 64, 16384).astype(np.int64)
+        n[:6] = [4095, 4096, 4097, 8191, 8192, 8193]
+    return workloads.make_spec(f"parts{kind}", (446, 102, kind), "bf16", 4, 1, 64, n - 1, np.ones_like(n))
+
+
+@pytest.mark.parametrize("kind", [2048, 3072, 4096])
+def test_decode_partition_sizes(kind):
+    # planted rows (one and two partitions, each +-1 token) and a spread of the
+    # others against the oracle; every row finite; a second call gives the same bits
+    import torch
+
+    from tests import gpu_pipeline as gp
+
+    spec = _partition_batch(kind)
+    gp.log(f"[parts] {kind}: S={spec.num_seqs} context={int(spec.seq_lens.sum())}")
+    run = gp.prepare(spec)
+    bits = run.out_bits().copy()
+    got = numerics.to_f64(bits, spec.dtype).reshape(spec.num_q_tokens, spec.num_q_heads, spec.head_dim)
+    seqs = sorted(set(range(6)) | set(_sample(spec, k=6)))
+    ref = op.run(spec, seqs=seqs)
+    ok, worst = gp.compare(got[seqs], ref.out[seqs], spec.dtype)
+    gp.log(f"[parts] {kind}: {len(seqs)} sequences, worst {worst:.3g}")
+    assert ok, f"partitions {kind}: worst error {worst}"
+    assert np.isfinite(got).all()
+    gp.attention(run)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits, run.out_bits())
