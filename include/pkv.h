@@ -154,7 +154,11 @@ int pkv_calib_stream_read(const void* buf, size_t bytes, void* sink, void* strea
  * q_len <= max_q_len, ceil(seq_len/16) <= bt_stride, table entries < num_blocks.
  * A sequence with seq_len = 0 and q_len >= 1 yields zeros.
  * Accumulation is fp32.  The output is bitwise reproducible run to run and
- * independent of where blocks sit in the pool.
+ * independent of where blocks sit in the pool.  Long decode rows are split into
+ * partitions of 1024 to 4096 tokens, a size the call chooses from the lengths of
+ * the whole batch (and 1024 under PKV_ATTN_SHARED_PREFIXES); the size sets the
+ * order of a row's fp32 sums, so the batch around a row, and that flag, can move
+ * its output by rounding (within the tolerance of the arithmetic), never more.
  */
 int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void* out, const void* q,
                         const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
@@ -165,9 +169,10 @@ int pkv_paged_attention(const pkv_cache_t* cache, int32_t layer, void* out, cons
 /* flags of pkv_paged_attention (any other bit: PKV_ERR_INVALID_ARGUMENT).
  * PKV_ATTN_SHARED_PREFIXES: rows share prefixes of blocks (parallel samples or
  *   beam candidates that point at the same blocks, prefix-cache hits; [blog]
- *   copy-on-write section).  A hint about speed only, never about results: the
- *   work is then ordered so that rows read shared blocks at about the same time
- *   (pkv_ba_num_shared() > 0 tells a caller that some block has several users). */
+ *   copy-on-write section).  A hint about speed: the work is then ordered so
+ *   that rows read shared blocks at about the same time, in 1024-token partitions
+ *   (pkv_ba_num_shared() > 0 tells a caller that some block has several users).
+ *   Results change by rounding at most (see the partition size above). */
 #define PKV_ATTN_SHARED_PREFIXES 1u
 
 /*

@@ -41,7 +41,6 @@ namespace pkv {
 constexpr int kPartBlocks = 64;  // blocks of the shortest decode partition (1024 tokens)
 constexpr int kPartChoices = 4;  // partitions of 1, 2, 3 or 4 x kPartBlocks blocks
 constexpr int kPartMax = kPartChoices * kPartBlocks;
-constexpr int kGpuCUs = 256;     // compute units of an MI355X
 constexpr int kPlanLevels = 2048;  // partition indices the plan orders items by (2M tokens)
 
 // ---------------------------------------------------------------------------
@@ -633,6 +632,22 @@ static int64_t split_rows(int64_t num_seqs, int64_t max_parts, int64_t num_q_hea
   return 2 * num_seqs * max_parts * num_q_heads;
 }
 
+// Compute units of the current device (queried once per device; 256 on an MI355X,
+// fewer in a partitioned mode), or 0 if the runtime cannot say.
+static int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  if (!cached[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 template <class DT, int D, int G, int CT>
 static int launch_ct(const AttnArgs& a, const DecodePlan& plan) {
   typedef typename DT::T T;
@@ -667,7 +682,9 @@ static int launch(const AttnArgs& a) {
   const bool two_only = a.uniform_q && widest > 16;
   // resident decode workgroups the plan balances over: those of the one-tile kernel,
   // unless every row takes two tiles
-  const int slots = kGpuCUs * (two_only ? decode_occupancy<DT, D, 2>() : decode_occupancy<DT, D, 1>());
+  const int cus = device_cus();
+  if (cus <= 0) return PKV_ERR_HIP;
+  const int slots = cus * (two_only ? decode_occupancy<DT, D, 2>() : decode_occupancy<DT, D, 1>());
   if (a.max_parts > 1) {
     // sequences may span several partitions: list the live (sequence, partition) items
     plan.counts = (int32_t*)a.ws_plan;
