@@ -379,55 +379,15 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
   }
 }
 
+// One work unit (item, KV head) of the decode kernel: the item's blocks of one row
+// for the G query heads of KV head it.h, merged over the four wavefronts through LDS.
 template <class DT, int D, int G, int CT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_occupancy<DT, D, CT>())))
-void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
-                   const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
-                   const int32_t* __restrict__ bt, int bt_stride,
-                   const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
-                   int num_kv_heads, float scale_log2, int max_parts, int max_q,
-                   float* __restrict__ ws_o, float* __restrict__ ws_ml, DecodePlan plan,
-                   int contiguous) {
+__device__ __forceinline__ void decode_unit(
+    const DecodeItem& it, const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
+    const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
+    const int32_t* __restrict__ bt, int bt_stride, int num_kv_heads, float scale_log2,
+    int max_parts, float* __restrict__ ws_o, float* __restrict__ ws_ml, int contiguous) {
   typedef Geo<DT, D> Gm;
-  // The work item's fields are pinned where they are loaded (an empty asm reads
-  // them), so that the metadata loads of a path issue together, in one round trip,
-  // and are not merged into one load after the paths join.
-  DecodeItem it;
-  if (plan.counts) {
-    const int live = plan.counts[CT == 1 ? 0 : 2];
-    int i, h;
-    if (plan.by_part) {
-      // head-major units in XCD runs: the rows reading one (block, head) tile run together
-      const int j = xcd_unit(blockIdx.x, live * num_kv_heads);
-      if (j < 0) return;
-      i = j % live;
-      h = j / live;
-    } else {
-      // longest first: the r-th workgroup of XCD x takes KV head r % H of the item at
-      // position x of round r / H of the list, counted from the other end in odd rounds
-      // (so no XCD takes the longest item of every round).  Past the list, and so last
-      // on every XCD, it returns.
-      const int x = blockIdx.x % kXcds, r = blockIdx.x / kXcds;
-      const int rd = r / num_kv_heads;
-      i = rd * kXcds + ((rd & 1) ? kXcds - 1 - x : x);
-      h = r % num_kv_heads;
-      if (i >= live) return;
-    }
-    it = plan.items[(CT == 1 ? 0 : (int64_t)plan.cap) + i];
-    asm volatile("" : "+s"(it.s), "+s"(it.b0), "+s"(it.b1), "+s"(it.qb), "+s"(it.q_len),
-                 "+s"(it.n), "+s"(it.part), "+s"(it.wrow));
-    it.h = h;
-    if (it.wrow >= 0) it.wrow += it.h * G;
-  } else {  // one partition per row: every sequence is an item
-    const int j = xcd_unit(blockIdx.x, plan.num_seqs * num_kv_heads);
-    if (j < 0) return;
-    const int s = j / num_kv_heads;
-    int q0 = qsl[s], q1 = qsl[s + 1], n = seq_lens[s];
-    asm volatile("" : "+s"(q0), "+s"(q1), "+s"(n));
-    it = DecodeItem{s, j % num_kv_heads, 0, kPartBlocks, q0, q1 - q0, n, 0, -1, 0};
-    const int cols = it.q_len * G;
-    if (it.q_len < 1 || it.q_len > max_q || cols > CT * 16 || cols <= (CT - 1) * 16) return;
-  }
   const int s = it.s, h = it.h, b0 = it.b0, qb = it.qb, q_len = it.q_len, n = it.n;
   const int cols = q_len * G;
   const int lane = threadIdx.x & 63;
@@ -557,6 +517,72 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
   }
 }
 
+template <class DT, int D, int G, int CT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_occupancy<DT, D, CT>())))
+void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,
+                   const typename DT::T* __restrict__ kp, const typename DT::T* __restrict__ vp,
+                   const int32_t* __restrict__ bt, int bt_stride,
+                   const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
+                   int num_kv_heads, float scale_log2, int max_parts, int max_q,
+                   float* __restrict__ ws_o, float* __restrict__ ws_ml, DecodePlan plan,
+                   int contiguous) {
+  // The work item's fields are pinned where they are loaded (an empty asm reads
+  // them), so that the metadata loads of a path issue together, in one round trip,
+  // and are not merged into one load after the paths join.
+  DecodeItem it;
+  if (plan.counts) {
+    // planned lists: workgroup b takes units v = b, b + grid, b + 2 grid, ... (grid a
+    // multiple of 8, so every unit of a workgroup maps to the same XCD), in list order
+    // on that XCD, until the list ends
+    const int live = plan.counts[CT == 1 ? 0 : 2];
+    for (int v = blockIdx.x;; v += gridDim.x) {
+      int i, h;
+      if (plan.by_part) {
+        // head-major units in XCD runs: the rows reading one (block, head) tile run together
+        const int j = xcd_unit(v, live * num_kv_heads);
+        if (j < 0) return;
+        i = j % live;
+        h = j / live;
+      } else {
+        // longest first: the r-th unit of XCD x is KV head r % H of the item at position
+        // x of round r / H of the list, counted from the other end in odd rounds (so no
+        // XCD takes the longest item of every round).  Past the list: done.
+        const int x = v % kXcds, r = v / kXcds;
+        const int rd = r / num_kv_heads;
+        i = rd * kXcds + ((rd & 1) ? kXcds - 1 - x : x);
+        h = r % num_kv_heads;
+        if (i >= live) return;
+      }
+      if (v != (int)blockIdx.x) __syncthreads();  // the last unit's LDS has been read
+      // one item per workgroup: the loop hides from the compiler that it is uniform
+      const DecodeItem& src = plan.items[(CT == 1 ? 0 : (int64_t)plan.cap) + uniform(i)];
+      it.s = uniform(src.s);
+      it.b0 = uniform(src.b0);
+      it.b1 = uniform(src.b1);
+      it.qb = uniform(src.qb);
+      it.q_len = uniform(src.q_len);
+      it.n = uniform(src.n);
+      it.part = uniform(src.part);
+      it.wrow = ((int64_t)uniform((int)(src.wrow >> 32)) << 32) | (uint32_t)uniform((int)src.wrow);
+      it.h = uniform(h);
+      if (it.wrow >= 0) it.wrow += it.h * G;
+      decode_unit<DT, D, G, CT>(it, q, out, kp, vp, bt, bt_stride, num_kv_heads, scale_log2,
+                                max_parts, ws_o, ws_ml, contiguous);
+    }
+  } else {  // one partition per row: every sequence is an item
+    const int j = xcd_unit(blockIdx.x, plan.num_seqs * num_kv_heads);
+    if (j < 0) return;
+    const int s = j / num_kv_heads;
+    int q0 = qsl[s], q1 = qsl[s + 1], n = seq_lens[s];
+    asm volatile("" : "+s"(q0), "+s"(q1), "+s"(n));
+    it = DecodeItem{s, j % num_kv_heads, 0, kPartBlocks, q0, q1 - q0, n, 0, -1, 0};
+    const int cols = it.q_len * G;
+    if (it.q_len < 1 || it.q_len > max_q || cols > CT * 16 || cols <= (CT - 1) * 16) return;
+    decode_unit<DT, D, G, CT>(it, q, out, kp, vp, bt, bt_stride, num_kv_heads, scale_log2,
+                              max_parts, ws_o, ws_ml, contiguous);
+  }
+}
+
 // Merge of the partitions of split rows, one workgroup per (merge entry = split
 // sequence and query token, KV head):
 //   o = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
@@ -648,15 +674,24 @@ static int device_cus() {
   return cached[dev];
 }
 
+// Workgroups of a planned decode launch per resident slot: enough that every unit of
+// a usual batch has its own workgroup (dealt by the hardware as slots free up), few
+// enough that the workgroups past the list (the grid is sized before the list is
+// known) cost little.
+constexpr int kDecodeOversub = 8;
+
 template <class DT, int D, int G, int CT>
-static int launch_ct(const AttnArgs& a, const DecodePlan& plan) {
+static int launch_ct(const AttnArgs& a, const DecodePlan& plan, int slots) {
   typedef typename DT::T T;
-  // grids sized for every sequence in every partition (whole rounds of 8 items for the
-  // longest-first mapping); the plan's counts cut them short
-  const int64_t items = (int64_t)a.max_parts * a.num_seqs;
-  const int64_t grid = plan.counts && !plan.by_part
-                           ? (items + kXcds - 1) / kXcds * kXcds * a.num_kv_heads
-                           : (items * a.num_kv_heads + kXcds - 1) / kXcds * kXcds;
+  // unplanned: one workgroup per (row, KV head); planned: every sequence in every
+  // partition at most, and at most kDecodeOversub per slot (workgroups then loop over
+  // units); the plan's counts cut the lists short
+  const int64_t units = (int64_t)a.max_parts * a.num_seqs * a.num_kv_heads;
+  int64_t grid = (units + kXcds - 1) / kXcds * kXcds;
+  if (plan.counts) {
+    const int64_t cap = ((int64_t)slots * kDecodeOversub + kXcds - 1) / kXcds * kXcds;
+    if (grid > cap) grid = cap;
+  }
   hipLaunchKernelGGL((decode_kernel<DT, D, G, CT>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                      (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt, a.bt_stride,
                      a.seq_lens, a.qsl, a.num_kv_heads, a.scale_log2, a.max_parts, a.max_q_len,
@@ -698,9 +733,11 @@ static int launch(const AttnArgs& a) {
                        a.num_kv_heads, slots,
                        (D + 2) * 4, kWaves * 2 * kBlock * D * DT::kBytes, plan);
   }
-  if (!two_only && launch_ct<DT, D, G, 1>(a, plan) != PKV_OK) return PKV_ERR_HIP;
+  if (!two_only && launch_ct<DT, D, G, 1>(a, plan, cus * decode_occupancy<DT, D, 1>()) != PKV_OK)
+    return PKV_ERR_HIP;
   if constexpr (kMaxCols > 16)
-    if (widest > 16 && launch_ct<DT, D, G, 2>(a, plan) != PKV_OK) return PKV_ERR_HIP;
+    if (widest > 16 && launch_ct<DT, D, G, 2>(a, plan, cus * decode_occupancy<DT, D, 2>()) != PKV_OK)
+      return PKV_ERR_HIP;
   if (a.max_parts > 1) {
     // merge entries: at most one per query token of the rows this kernel takes
     const int64_t qmax = a.max_q_len < kMaxCols / G ? a.max_q_len : kMaxCols / G;
@@ -784,7 +821,7 @@ static int attention_impl(const pkv_cache_t* cache, int32_t layer, void* out, co
   if (cache->dtype == PKV_F32 && cache->head_dim == 256) return PKV_ERR_UNSUPPORTED;
   // the decode and merge grids (padded to whole XCD rounds) must fit their limit
   const int64_t per_seq = max_partitions(max_seq_len) > 32 ? max_partitions(max_seq_len) : 32;
-  if (((int64_t)num_seqs * per_seq + kXcds) * cache->num_kv_heads > 0x7fffffff)
+  if ((int64_t)num_seqs * cache->num_kv_heads * per_seq + kXcds > 0x7fffffff)
     return PKV_ERR_INVALID_ARGUMENT;
   const size_t need = pkv_paged_attention_workspace_bytes(num_seqs, num_q_tokens, max_seq_len,
                                                           num_q_heads, cache->head_dim);
