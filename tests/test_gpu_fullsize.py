@@ -116,3 +116,40 @@ def test_decode_partition_sizes(kind):
     gp.attention(run)
     torch.cuda.synchronize()
     assert np.array_equal(bits, run.out_bits())
+
+
+@pytest.mark.parametrize("kind", ["one-tile", "two-tile"])
+def test_decode_units_beyond_the_grid_cap(kind):
+    # A planned decode launch has at most 8 workgroups per resident slot (6,144 for
+    # the one-tile kernel at 3 workgroups per CU, 4,096 for the two-tile kernel at 2);
+    # here the (item, KV head) units outnumber them, so workgroups take several units
+    # one after another.  A few rows past 1024 tokens make the call planned.
+    import torch
+
+    from tests import gpu_pipeline as gp
+
+    rng = np.random.default_rng([446, 103, len(kind)])
+    if kind == "one-tile":  # 7,000 decode rows x 1 KV head, head_dim 64
+        n = rng.integers(1, 40, size=7000, endpoint=True)
+        n[rng.choice(7000, size=4, replace=False)] = [1025, 2048, 3000, 4097]
+        spec = workloads.make_spec("cap1", (446, 103, 1), "bf16", 4, 1, 64, n - 1, np.ones_like(n))
+    else:  # 640 verify rows of 5 tokens x 8 KV heads (20 columns: two tiles)
+        n = rng.integers(6, 200, size=640, endpoint=True)
+        n[rng.choice(640, size=4, replace=False)] = [1030, 2050, 3000, 4100]
+        q = np.full(640, 5, dtype=np.int64)
+        spec = workloads.make_spec("cap2", (446, 103, 2), "bf16", 32, 8, 128, n - q, q)
+    gp.log(f"[cap] {kind}: S={spec.num_seqs} context={int(spec.seq_lens.sum())}")
+    run = gp.prepare(spec)
+    bits = run.out_bits().copy()
+    got = numerics.to_f64(bits, spec.dtype).reshape(spec.num_q_tokens, spec.num_q_heads, spec.head_dim)
+    seqs = sorted(set(int(s) for s in np.argsort(spec.seq_lens)[-4:]) |
+                  set(int(s) for s in rng.choice(spec.num_seqs, size=24, replace=False)))
+    ref = op.run(spec, seqs=seqs)
+    rows = np.concatenate([np.arange(spec.query_start_loc[s], spec.query_start_loc[s + 1]) for s in seqs])
+    ok, worst = gp.compare(got[rows], ref.out[rows], spec.dtype)
+    gp.log(f"[cap] {kind}: {len(seqs)} sequences, worst {worst:.3g}")
+    assert ok, f"{kind}: worst error {worst}"
+    assert np.isfinite(got).all()
+    gp.attention(run)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits, run.out_bits())
