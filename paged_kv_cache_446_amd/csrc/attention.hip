@@ -64,7 +64,7 @@ constexpr int decode_occupancy() {
 // KV head h, blocks [b0, b1) (partition part of the row), the row's first query
 // row qb, its query tokens and sequence length, and the workspace row of
 // (this partition, token 0, head h*G) if the row is split over partitions
-// (wrow < 0 otherwise).  One 48-byte record, read with two scalar loads.
+// (wrow < 0 otherwise).  One 48-byte record per item.
 struct alignas(16) DecodeItem {
   int32_t s, h, b0, b1, qb, q_len, n, part;
   int64_t wrow, unused;
@@ -72,7 +72,7 @@ struct alignas(16) DecodeItem {
 
 // Work lists of one call, written by decode_plan_kernel: the items of one-tile
 // rows (class 1) and of two-tile rows (class 2), with h = 0, longest first
-// (blocks per item, descending), or partition-major when the caller says that
+// (blocks per item in bins of 4, descending), or partition-major when the caller says that
 // rows share prefixes of blocks (PKV_ATTN_SHARED_PREFIXES): partition 0 of every
 // row, then partition 1 of every row that has one, and so on.  The order within
 // one length or partition index is not kept.
@@ -526,9 +526,9 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
                    int num_kv_heads, float scale_log2, int max_parts, int max_q,
                    float* __restrict__ ws_o, float* __restrict__ ws_ml, DecodePlan plan,
                    int contiguous) {
-  // The work item's fields are pinned where they are loaded (an empty asm reads
-  // them), so that the metadata loads of a path issue together, in one round trip,
-  // and are not merged into one load after the paths join.
+  // The work item's fields are held in scalar registers: read with readfirstlane in
+  // the planned loop, pinned by an empty asm where the unplanned path loads them (so
+  // that its metadata loads issue together, in one round trip).
   DecodeItem it;
   if (plan.counts) {
     // planned lists: workgroup b takes units v = b, b + grid, b + 2 grid, ... (grid a
