@@ -366,6 +366,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--num-seqs", type=int, default=None,
+                    help="decode workloads c2/c3 only: a batch of this many rows drawn from the "
+                         "same length distribution (its own seed stream); default: the "
+                         "workload's own batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
@@ -401,7 +405,12 @@ def main():
     if args.config == "beam":
         return bench_beam(args)
     dev = "cuda:0"
-    spec = workloads.named_spec(args.config)
+    if args.num_seqs is not None:
+        if args.config not in ("c2", "c3") or args.num_seqs < 1:
+            raise SystemExit("--num-seqs applies to the decode workloads c2 and c3 (>= 1 rows)")
+        spec = workloads.scaled_spec(args.config, num_seqs=args.num_seqs, variant=11)
+    else:
+        spec = workloads.named_spec(args.config)
     log(f"workload {args.config}: S={spec.num_seqs} context tokens={int(spec.seq_lens.sum())} "
         f"pool blocks={spec.num_blocks}")
 
@@ -583,7 +592,9 @@ def main():
         "dtype": spec.dtype,
         "data": "synthetic (seeded N(0,1) K/V/Q, seeded block placement)",
         "config": {
-            "workload": WORKLOAD_NAMES[args.config],
+            "workload": WORKLOAD_NAMES[args.config] + (
+                "" if args.num_seqs is None else
+                f" (batch of {args.num_seqs} rows from the same length distribution)"),
             "num_seqs": S,
             "query_tokens": spec.num_q_tokens,
             "context_tokens": int(spec.seq_lens.sum()),
@@ -611,8 +622,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic() if (args.config, args.placement, args.kernel) ==
-            ("c3", "random", "paged") else None,
+            "traffic": measured_traffic() if (args.config, args.placement, args.kernel,
+                                               args.num_seqs) == ("c3", "random", "paged", None)
+            else None,
             "algorithmic_bytes_per_launch": attn_bytes,
             "avg_launch_us": round(attn_avg * 1e3, 2),
             # a plain 4 GiB read stream on the same GPU: the practical read rate
