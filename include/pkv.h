@@ -287,17 +287,21 @@ int pkv_seq_free(pkv_ba_t* ba, const int32_t* table, int32_t nblk);
  * instead of recomputing them ([blog] advanced features and V1: prefix caching
  * by hash, on by default; [devpress] sharing section: prompt caching).
  *
- * A full block is sealed with the 16 token ids it holds and its parent (the
- * block before it in the sequence, -1 for the first).  A sealed block stays in
- * the cache while it is in use and after its count drops to zero; the free
- * pool hands out the block released longest ago first, and a cached block
- * taken that way leaves the cache (least-recently-released eviction).  The
- * contents of a sealed block must not change.
+ * A full block caches the K/V of one exact prompt prefix (the K/V of a token
+ * depend on every token before it).  It is sealed with the 16 token ids it
+ * holds and its parent: the cached block of the prefix before it (-1 for a
+ * prompt's first block).  A sealed block stays in the cache while it is in use
+ * and after its count drops to zero; the free pool hands out the block
+ * released longest ago first, and a cached block taken that way leaves the
+ * cache together with every block cached below it (their prefixes begin with
+ * the evicted one).  The contents of a sealed block must not change, and a
+ * block appears at most once in a table.
  */
 
 /* Chained 64-bit hash of one block's 16 token ids after a parent hash (0 for
- * the first block).  Lookups locate candidates with it and then compare parent
- * and token ids exactly, so a hash collision cannot produce a wrong hit. */
+ * the first block).  Lookups locate candidates with it and then compare the
+ * parent block and the token ids exactly; a parent is always a live cached
+ * prefix, so a hash collision cannot produce a wrong hit. */
 uint64_t pkv_prefix_hash(uint64_t parent_hash, const int32_t* tokens16);
 
 /* Start a new sequence from the cache: walk the full blocks of its prompt
@@ -311,9 +315,10 @@ int pkv_seq_cache_lookup(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens
 
 /* Register the full blocks of a sequence (table[0..nblk) holding
  * tokens[0..num_tokens)) in the cache once their K/V are written.  Blocks
- * already cached must hold the same tokens after the same parent
- * (PKV_ERR_INVALID_ARGUMENT otherwise, and nothing changes); a block whose
- * content is cached under another block stays out of the cache. */
+ * already cached must hold the same prefix (PKV_ERR_INVALID_ARGUMENT
+ * otherwise, and nothing changes); a block whose prefix is cached in another
+ * block stays out of the cache, and the next block is cached after that other
+ * block. */
 int pkv_seq_cache_seal(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens,
                        const int32_t* table, int32_t nblk);
 

@@ -204,25 +204,41 @@ class BlockAllocatorModel:
             raise
 
     # ---- prefix cache -------------------------------------------------------
-    # A full block is cached under the exact key (parent block, its 16 token ids):
-    # a later prompt starting with the same tokens finds the same chain of blocks
-    # (blog.mckayzhao.com/?p=56, advanced features and V1 sections: hash-based
-    # automatic prefix caching; devpress page, sharing section).  Cached blocks
-    # stay findable after their count drops to zero; the free queue hands out the
-    # block released longest ago first, which leaves the cache.
+    # A request whose prompt starts with an earlier request's tokens reuses the K/V
+    # blocks computed for them (blog.mckayzhao.com/?p=56, advanced features and V1
+    # sections: automatic prefix caching; devpress page, sharing section).  The K/V
+    # of a token depend on every token before it, so a full block caches the K/V of
+    # one exact prefix: logical block j of a prompt is keyed by the tuple of ALL of
+    # the prompt's tokens 0 .. 16(j+1)-1.  Cached blocks stay findable after their
+    # count drops to zero; the free queue hands out the block released longest ago
+    # first, and a cached block taken that way leaves the cache together with every
+    # cached key that extends its key (a lookup walks a prompt's blocks from the
+    # first one and stops at the first miss, so what is cached below an evicted
+    # block is dropped with it: the plainest policy, which the pages leave open).
 
     def _cache(self):
         if not hasattr(self, "key_of"):
-            self.key_of = {}   # block -> key
+            self.key_of = {}   # block -> key (full prefix tuple)
             self.block_of = {}  # key -> block
         return self.key_of, self.block_of
 
     def _take_front(self) -> int:
         b = self.free.popleft()
-        key_of, block_of = self._cache()
-        if b in key_of:
-            del block_of[key_of.pop(b)]
+        if b in self._cache()[0]:
+            self._evict(b)
         return b
+
+    def _evict(self, b):
+        """Drop cached block b and every cached key that extends its key."""
+        key_of, block_of = self._cache()
+        gone = key_of[b]
+        for key in [k for k in block_of if k[:len(gone)] == gone]:
+            del key_of[block_of.pop(key)]
+
+    @staticmethod
+    def _prefix_key(tokens, table, j):
+        """Key of logical block j of a prompt: all of its tokens up to that block's end."""
+        return tuple(tokens[:(j + 1) * BLOCK_SIZE])
 
     def cache_lookup(self, tokens, table) -> int:
         key_of, block_of = self._cache()
@@ -230,8 +246,7 @@ class BlockAllocatorModel:
         n = min(len(tokens) // BLOCK_SIZE, len(table))
         j = 0
         while j < n:
-            key = (int(table[j - 1]) if j else -1, tuple(tokens[j * BLOCK_SIZE:(j + 1) * BLOCK_SIZE]))
-            b = block_of.get(key)
+            b = block_of.get(self._prefix_key(tokens, table, j))
             if b is None:
                 break
             if self.ref[b] == 0:
@@ -245,8 +260,7 @@ class BlockAllocatorModel:
         key_of, block_of = self._cache()
         tokens = [int(t) for t in tokens]
         n = min(len(tokens) // BLOCK_SIZE, nblk)
-        keys = [(int(table[j - 1]) if j else -1, tuple(tokens[j * BLOCK_SIZE:(j + 1) * BLOCK_SIZE]))
-                for j in range(n)]
+        keys = [self._prefix_key(tokens, table, j) for j in range(n)]
         for j in range(n):
             b = int(table[j])
             self._check_id(b)

@@ -16,12 +16,16 @@
  *
  * Prefix cache (hash-based automatic prefix caching: blog page, advanced
  * features and V1 sections; devpress page, sharing section, prompt caching):
- * a full block can be sealed with the 16 token ids it holds and its parent
- * (the block before it in the sequence).  Sealed blocks stay findable after
- * their count drops to zero, until allocation takes them from the front of the
- * free queue (least recently released first).  A lookup walks a new prompt's
- * full blocks, finding each by a chained 64-bit hash and verifying parent and
- * token ids exactly.
+ * a full block caches the K/V of one exact prompt prefix.  It is sealed with
+ * the 16 token ids it holds and its parent: the cached block of the prefix
+ * before it (-1 for a prompt's first block).  Sealed blocks form a forest in
+ * which a block's parent is always sealed: when allocation takes a sealed block
+ * from the front of the free queue (least recently released first), the block
+ * and everything sealed below it leave the cache together.  A lookup walks a
+ * new prompt's full blocks, locating each candidate by a chained 64-bit hash
+ * and accepting it only if its parent is the block found one step earlier and
+ * its token ids are equal; a parent id names a live cached prefix, so a hit is
+ * exact whatever the hash does.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -40,7 +44,8 @@ struct pkv_ba {
   /* prefix cache */
   uint8_t* sealed;   /* [num_blocks] 1 if the block is in the cache */
   uint64_t* hash;    /* [num_blocks] chained hash of the block's tokens */
-  int32_t* parent;   /* [num_blocks] previous block of the sequence, -1 for the first */
+  int32_t* parent;   /* [num_blocks] cached block of the prefix before, -1 for the first */
+  int32_t* first_child, *next_sib, *prev_sib; /* [num_blocks] sealed children of a sealed block */
   int32_t* tokens;   /* [num_blocks][16] token ids */
   int32_t* slot;     /* [hcap] open-addressing table of sealed block ids; -1 empty, -2 deleted */
   int64_t hcap;      /* power of two >= 2 * num_blocks */
@@ -121,23 +126,53 @@ static void rehash(pkv_ba_t* ba) {
     if (ba->sealed[b]) slot_insert(ba, b);
 }
 
+/* parent: a sealed block or -1 */
 static void seal(pkv_ba_t* ba, int32_t b, uint64_t h, int32_t parent, const int32_t* tokens) {
   if (4 * (ba->num_sealed + 1 + ba->num_deleted) > 3 * ba->hcap) rehash(ba);
   ba->hash[b] = h;
   slot_insert(ba, b);
   ba->sealed[b] = 1;
   ba->parent[b] = parent;
+  ba->first_child[b] = -1;
+  ba->prev_sib[b] = -1;
+  ba->next_sib[b] = parent >= 0 ? ba->first_child[parent] : -1;
+  if (ba->next_sib[b] >= 0) ba->prev_sib[ba->next_sib[b]] = b;
+  if (parent >= 0) ba->first_child[parent] = b;
   memcpy(ba->tokens + (int64_t)b * PKV_BLOCK_SIZE, tokens, PKV_BLOCK_SIZE * sizeof(int32_t));
   ba->num_sealed++;
 }
 
-static void unseal(pkv_ba_t* ba, int32_t b) {
+static void drop_from_table(pkv_ba_t* ba, int32_t b) {
   int64_t i = (int64_t)(ba->hash[b] & (uint64_t)(ba->hcap - 1));
   while (ba->slot[i] != b) i = (i + 1) & (ba->hcap - 1);
   ba->slot[i] = -2;
   ba->num_deleted++;
   ba->sealed[b] = 0;
   ba->num_sealed--;
+}
+
+/* Remove a sealed block and every block sealed below it from the cache: their
+ * prefixes begin with the evicted one, which a lookup can no longer walk. */
+static void unseal(pkv_ba_t* ba, int32_t root) {
+  const int32_t p = ba->parent[root];
+  if (p >= 0) { /* unlink root from its parent's children */
+    const int32_t pv = ba->prev_sib[root], nx = ba->next_sib[root];
+    if (pv >= 0) ba->next_sib[pv] = nx; else ba->first_child[p] = nx;
+    if (nx >= 0) ba->prev_sib[nx] = pv;
+  }
+  /* pre-order walk of the subtree; the links below root are read, not changed (an
+   * unsealed block's links are reset when it is sealed again) */
+  int32_t b = root;
+  for (;;) {
+    drop_from_table(ba, b);
+    if (ba->first_child[b] >= 0) {
+      b = ba->first_child[b];
+      continue;
+    }
+    while (b != root && ba->next_sib[b] < 0) b = ba->parent[b];
+    if (b == root) break;
+    b = ba->next_sib[b];
+  }
 }
 
 int64_t pkv_blocks_for_tokens(int64_t n, int32_t block_size) {
@@ -161,10 +196,13 @@ int pkv_ba_create(int32_t num_blocks, int32_t block_size, const int32_t* free_or
   ba->sealed = (uint8_t*)calloc(nb, 1);
   ba->hash = (uint64_t*)calloc(nb, sizeof(uint64_t));
   ba->parent = (int32_t*)calloc(nb, sizeof(int32_t));
+  ba->first_child = (int32_t*)calloc(nb, sizeof(int32_t));
+  ba->next_sib = (int32_t*)calloc(nb, sizeof(int32_t));
+  ba->prev_sib = (int32_t*)calloc(nb, sizeof(int32_t));
   ba->tokens = (int32_t*)calloc(nb * PKV_BLOCK_SIZE, sizeof(int32_t));
   ba->slot = (int32_t*)malloc((size_t)ba->hcap * sizeof(int32_t));
   if (!ba->ref || !ba->next || !ba->prev || !ba->sealed || !ba->hash || !ba->parent ||
-      !ba->tokens || !ba->slot) {
+      !ba->first_child || !ba->next_sib || !ba->prev_sib || !ba->tokens || !ba->slot) {
     pkv_ba_destroy(ba);
     return PKV_ERR_INVALID_ARGUMENT;
   }
@@ -194,6 +232,9 @@ void pkv_ba_destroy(pkv_ba_t* ba) {
   free(ba->sealed);
   free(ba->hash);
   free(ba->parent);
+  free(ba->first_child);
+  free(ba->next_sib);
+  free(ba->prev_sib);
   free(ba->tokens);
   free(ba->slot);
   free(ba);
@@ -475,25 +516,42 @@ int pkv_seq_cache_seal(pkv_ba_t* ba, const int32_t* tokens, int32_t num_tokens,
   const int32_t n = full < nblk ? full : nblk;
   int rc = check_table(ba, table, n);
   if (rc != PKV_OK) return rc;
-  /* verify first, then seal: all or nothing */
+  /* Both passes walk the prompt's prefixes; `cur` is the cached block of the prefix
+   * before block j: table[j - 1] if it is (or will be) sealed, else the block that
+   * already caches the same prefix.  Verify first, then seal: all or nothing. */
   uint64_t h = 0;
+  int32_t cur = -1;
   for (int32_t j = 0; j < n; ++j) {
     const int32_t* tk = tokens + (int64_t)j * PKV_BLOCK_SIZE;
-    const int32_t b = table[j], parent = j ? table[j - 1] : -1;
+    const int32_t b = table[j];
     h = pkv_prefix_hash(h, tk);
-    if (ba->sealed[b] && (ba->hash[b] != h || ba->parent[b] != parent ||
-                          memcmp(ba->tokens + (int64_t)b * PKV_BLOCK_SIZE, tk,
-                                 PKV_BLOCK_SIZE * sizeof(int32_t))))
-      return PKV_ERR_INVALID_ARGUMENT; /* a cached block must keep its contents */
+    if (ba->sealed[b]) {
+      if (ba->hash[b] != h || ba->parent[b] != cur ||
+          memcmp(ba->tokens + (int64_t)b * PKV_BLOCK_SIZE, tk, PKV_BLOCK_SIZE * sizeof(int32_t)))
+        return PKV_ERR_INVALID_ARGUMENT; /* a cached block must keep its contents */
+      cur = b;
+    } else {
+      const int32_t f = find_sealed(ba, h, cur, tk);
+      cur = f >= 0 ? f : b;
+    }
   }
   h = 0;
+  cur = -1;
   for (int32_t j = 0; j < n; ++j) {
     const int32_t* tk = tokens + (int64_t)j * PKV_BLOCK_SIZE;
-    const int32_t b = table[j], parent = j ? table[j - 1] : -1;
+    const int32_t b = table[j];
     h = pkv_prefix_hash(h, tk);
-    if (ba->sealed[b]) continue;
-    if (find_sealed(ba, h, parent, tk) >= 0) continue; /* the same content is cached already */
-    seal(ba, b, h, parent, tk);
+    if (ba->sealed[b]) {
+      cur = b;
+      continue;
+    }
+    const int32_t f = find_sealed(ba, h, cur, tk);
+    if (f >= 0) { /* the same prefix is cached in another block already */
+      cur = f;
+      continue;
+    }
+    seal(ba, b, h, cur, tk);
+    cur = b;
   }
   return PKV_OK;
 }

@@ -1,11 +1,12 @@
 """Hash-based automatic prefix caching in the host allocator (CPU only).
 
 The C allocator must agree call for call with the oracle's model, which keys
-cached blocks exactly by (parent block, 16 token ids) with no hashing; and the
-rules the pages state must hold: a repeated prompt reuses the earlier
-request's full blocks (the ~10,000-token prefix example of the blog page's
-advanced-features section), and the cache keeps what was released most
-recently.
+a cached block by the whole token prefix it holds the K/V of, with no hashing;
+every hit must return a block holding exactly the prompt's own prefix (tracked
+independently of both); and the rules the pages state must hold: a repeated
+prompt reuses the earlier request's full blocks (the ~10,000-token prefix
+example of the blog page's advanced-features section), and the cache keeps
+what was released most recently.
 """
 
 import numpy as np
@@ -143,7 +144,7 @@ def test_cache_evicts_the_block_released_longest_ago(impl):
     t = a.new_table(4)
     assert a.cache_lookup(p1, t) == 0          # p1's chain is broken at its first block
     assert a.cache_lookup(p2, t) == 2          # p2 is still whole
-    assert a.num_cached() == 3
+    assert a.num_cached() == 2                 # p1's second block left with its first
 
 
 @pytest.mark.parametrize("impl", ["c", "model"])
@@ -196,3 +197,175 @@ def test_shared_block_count_follows_forks_cow_and_frees(impl):
     a.free_seq(t2, nb2)
     assert a.num_shared() == 0 and a.num_free() == 16
 
+
+
+# ---- exactness: a hit must return the K/V of exactly the prompt's own prefix ------
+# The pages define prefix caching as reusing the K/V already computed for the same
+# beginning of a prompt (blog page, advanced features: prefix caching; intro page,
+# features: automatic prefix caching).  The K/V of a token depend on every token
+# before it, so a block computed under one prefix is a wrong hit for any other.
+
+def _words(seed, n_words=5):
+    rng = np.random.default_rng(seed)
+    return [rng.integers(0, 1000, size=16).astype(np.int32) for _ in range(n_words)]
+
+
+@pytest.mark.parametrize("impl", ["c", "model"])
+def test_evicted_parent_does_not_revive_its_child(impl):
+    # seal [A, B]; free it; the block that held A is taken and sealed as [X]; a
+    # lookup of [X, B] may reuse X's block only: B's block holds the K/V of B after A
+    A, B, X = _words(1, 3)
+    a = _new_c(2, None) if impl == "c" else oalloc.BlockAllocatorModel(2)
+    t1, nb1, _, _ = _serve(a, np.concatenate([A, B]), 4)
+    a.free_seq(t1, nb1)
+    assert a.num_cached() == 2
+    t2, nb2, hit, _ = _serve(a, X, 4)
+    assert hit == 0 and t2[0] == t1[0]          # A's block, the one released first, is reused
+    t = a.new_table(4)
+    assert a.cache_lookup(np.concatenate([X, B]), t) == 1
+    assert t[0] == t2[0]
+    # A computed again in another block: [A, B] finds A only (B's block left with A's)
+    a.free_seq(t, 1)
+    a.free_seq(t2, nb2)
+    t3, nb3, hit3, _ = _serve(a, A, 4)
+    assert hit3 == 0
+    t4 = a.new_table(4)
+    assert a.cache_lookup(np.concatenate([A, B]), t4) == 1 and t4[0] == t3[0]
+
+
+@pytest.mark.parametrize("impl", ["c", "model"])
+def test_child_sealed_under_the_block_that_caches_its_prefix(impl):
+    # two requests compute [A] at the same time; the first seals its A, the second's
+    # copy of A stays out of the cache, and the second's next block B is cached after
+    # the first's A: a later [A, B] reuses both
+    A, B = _words(2, 2)
+    a = _new_c(8, None) if impl == "c" else oalloc.BlockAllocatorModel(8)
+    p = np.concatenate([A, B])
+    t1 = a.new_table(4)
+    nb1, _, _, _ = a.append_slots(t1, 0, 0, 16)
+    t2 = a.new_table(4)
+    nb2, _, _, _ = a.append_slots(t2, 0, 0, 32)
+    a.cache_seal(A, t1, nb1)
+    a.cache_seal(p, t2, nb2)
+    assert a.num_cached() == 2  # t1's A and t2's B
+    t = a.new_table(4)
+    assert a.cache_lookup(p, t) == 2
+    assert t[0] == t1[0] and t[1] == t2[1]
+
+
+class _Truth:
+    """What each physical block holds: the exact token prefix its K/V were
+    computed for (written through its slots, or copied by copy-on-write)."""
+
+    def __init__(self):
+        self.held = {}
+
+    def wrote(self, table, first_blk, nblk, tokens):
+        for j in range(first_blk, nblk):
+            self.held[int(table[j])] = tuple(int(x) for x in tokens[:min(len(tokens), 16 * (j + 1))])
+
+    def check_hits(self, table, hit, tokens):
+        for j in range(hit):
+            assert self.held.get(int(table[j])) == tuple(int(x) for x in tokens[:16 * (j + 1)]), \
+                f"block {int(table[j])} at logical {j} holds another prefix"
+
+
+def _recombining_requests(seed, alloc, n_ops=600, cap=12):
+    """Prompts built from a few 16-token words in random order, so later prompts
+    recombine blocks of earlier ones; a small pool keeps evicting.  Every hit is
+    checked against what its block really holds."""
+    rng = np.random.default_rng(seed)
+    words = _words(seed + 100, 4)  # prompts: a first word, then words from the first two
+    truth = _Truth()
+    live, log = [], []
+    for _ in range(n_ops):
+        op = int(rng.integers(0, 7))
+        try:
+            if op <= 1 or not live:
+                n_w = int(rng.integers(1, 5))
+                tail = int(rng.integers(0, 12)) * int(rng.integers(0, 2))
+                prompt = np.concatenate([words[int(rng.integers(0, 4 if w == 0 else 2))] for w in range(n_w)]
+                                        + [rng.integers(0, 1000, size=tail).astype(np.int32)])
+                t = alloc.new_table(cap)
+                hit = alloc.cache_lookup(prompt, t)
+                truth.check_hits(t, hit, prompt)
+                try:
+                    nb, _, slots, _ = alloc.append_slots(t, hit, hit * 16, len(prompt) - hit * 16)
+                except oalloc.AllocError if isinstance(alloc, oalloc.BlockAllocatorModel) else RuntimeError:
+                    alloc.free_seq(t, hit)  # the request cannot start: give its hits back
+                    raise
+                truth.wrote(t, hit, nb, prompt)
+                alloc.cache_seal(prompt, t, nb)
+                log.append(("request", hit, t[:nb].tolist()))
+                if op == 0:
+                    alloc.free_seq(t, nb)  # served and finished at once
+                else:
+                    live.append([t, nb, list(prompt)])
+            elif op == 2:
+                i = int(rng.integers(0, len(live)))
+                t, nb, toks = live[i]
+                n_new = int(rng.integers(1, 20))
+                old_nb = nb
+                nb2, _, slots, pairs = alloc.append_slots(t, nb, len(toks), n_new)
+                for src, dst in pairs:
+                    truth.held[int(dst)] = truth.held.get(int(src))
+                toks.extend(int(x) for x in rng.integers(0, 1000, size=n_new))
+                truth.wrote(t, max(old_nb - 1, 0), nb2, toks)
+                live[i][1] = nb2
+                alloc.cache_seal(np.array(toks, dtype=np.int32), t, nb2)
+                log.append(("grow", slots.tolist(), pairs.tolist()))
+            elif op == 3:
+                i = int(rng.integers(0, len(live)))
+                t, nb, toks = live[i]
+                live.append([alloc.fork(t, nb), nb, list(toks)])
+                log.append(("fork",))
+            else:
+                t, nb, toks = live.pop(int(rng.integers(0, len(live))))
+                alloc.free_seq(t, nb)
+                log.append(("finish", nb))
+        except AssertionError:
+            raise
+        except Exception as e:
+            log.append(("error", type(e).__name__ if not hasattr(e, "name") else e.name))
+        log.append(("state", alloc.num_free(), alloc.num_cached(), alloc.num_shared()))
+    return log
+
+
+_STREAMS = [(seed, blocks) for seed in range(21, 33) for blocks in (8, 12)]
+
+
+@pytest.mark.parametrize("seed,blocks", _STREAMS)
+def test_recombined_prompts_hit_only_their_own_prefix(seed, blocks):
+    order = np.random.default_rng(seed + 3).permutation(blocks).astype(np.int32)
+    m = _recombining_requests(seed, oalloc.BlockAllocatorModel(blocks, free_order=order))
+    a = _recombining_requests(seed, _new_c(blocks, order))
+    m = [(x[0], _ERR[x[1]]) if x[0] == "error" else x for x in m]
+    assert a == m
+    hits = [x[1] for x in a if x[0] == "request"]
+    assert sum(h > 0 for h in hits) > 20 and max(hits) >= 2  # the cache was reached, chains too
+
+
+class _KeyedByParentBlock(oalloc.BlockAllocatorModel):
+    """A planted mistake: blocks keyed by (parent block id, own 16 tokens), and an
+    eviction that drops only the evicted block's own key."""
+
+    @staticmethod
+    def _prefix_key(tokens, table, j):
+        return (int(table[j - 1]) if j else -1, tuple(tokens[j * 16:(j + 1) * 16]))
+
+    def _evict(self, b):
+        key_of, block_of = self._cache()
+        del block_of[key_of.pop(b)]
+
+
+def test_recombined_streams_catch_a_stale_child_hit():
+    # the streams above reach a child whose parent block was evicted and reused: the
+    # per-block-id keying returns that child for the new parent, and the check fails
+    caught = 0
+    for seed, blocks in _STREAMS:
+        order = np.random.default_rng(seed + 3).permutation(blocks).astype(np.int32)
+        try:
+            _recombining_requests(seed, _KeyedByParentBlock(blocks, free_order=order))
+        except AssertionError:
+            caught += 1
+    assert caught >= 5
