@@ -116,8 +116,19 @@ def measured_traffic():
     return int(m.group(1))
 
 
-def cpu_baseline(spec, out_bits, target_s):
-    """The oracle (as it stands) on a bounded sample of the same workload."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(spec, out_bits, target_s, one_thread=True):
+    """The oracle (as it stands) on a bounded sample of the same workload, on every
+    core this process may use (BLAS threads set to that count), and on one thread."""
     import threadpoolctl
 
     from oracle import allocator as oalloc
@@ -135,19 +146,26 @@ def cpu_baseline(spec, out_bits, target_s):
     tables = flow.padded_tables(pad=0)
     q = spec.all_q_bits()
     qsl = spec.query_start_loc
-    reps, elapsed, ref = 0, 0.0, None
-    while elapsed < target_s and reps < 50:
-        t0 = time.perf_counter()
-        ref = oattn.paged_attention(q, kp, vp, tables, spec.seq_lens, qsl, spec.scale, spec.dtype,
-                                    seqs=sample)
-        elapsed += time.perf_counter() - t0
-        reps += 1
+    cores = len(os.sched_getaffinity(0))
+
+    def timed(threads, budget_s):
+        reps, elapsed, ref = 0, 0.0, None
+        with threadpoolctl.threadpool_limits(limits=threads):
+            while elapsed < budget_s and reps < 50:
+                t0 = time.perf_counter()
+                ref = oattn.paged_attention(q, kp, vp, tables, spec.seq_lens, qsl, spec.scale,
+                                            spec.dtype, seqs=sample)
+                elapsed += time.perf_counter() - t0
+                reps += 1
+        return reps, elapsed, ref
+
+    reps, elapsed, ref = timed(cores, target_s)
     kv_sample = int(spec.seq_lens[sample].sum()) * spec.num_kv_heads * spec.head_dim * 2 * spec.elem_bytes
     tok_sample = int(sum(qsl[s + 1] - qsl[s] for s in sample))
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     # parity of the GPU rows of the sample against the oracle
     got = numerics.to_f64(out_bits, spec.dtype).reshape(ref.shape)
     rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in sample])
+    assert len(rows) > 0 and not np.isnan(ref[rows]).any()
     diff = np.abs(got[rows] - ref[rows])
     if spec.dtype == "f32":
         worst = float((diff.max(axis=-1) / np.abs(ref[rows]).max(axis=-1)).max())
@@ -159,11 +177,19 @@ def cpu_baseline(spec, out_bits, target_s):
         "value": round(kv_sample * reps / elapsed / 1e9, 4),
         "unit": "GB/s",
         "tokens_per_s": round(tok_sample * reps / elapsed, 2),
-        "cores": int(threads),
+        "cores": cores,
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
-        "sample": f"{len(sample)} of {S} sequences (every 8th), {int(spec.seq_lens[sample].sum())} context tokens, "
-                  f"{reps} pass(es) in {elapsed:.1f} s, fp64 NumPy",
+        "sample": f"{len(sample)} of {S} sequences{' (every 8th)' if S >= 64 else ''}, "
+                  f"{int(spec.seq_lens[sample].sum())} context tokens, "
+                  f"{reps} pass(es) in {elapsed:.1f} s, fp64 NumPy, BLAS threads = {cores} "
+                  f"(the cores of os.sched_getaffinity)",
     }
+    if one_thread:
+        reps1, elapsed1, _ = timed(1, target_s / 2)
+        base["one_thread"] = {"value": round(kv_sample * reps1 / elapsed1 / 1e9, 4), "unit": "GB/s",
+                              "tokens_per_s": round(tok_sample * reps1 / elapsed1, 2),
+                              "sample": f"the same sample, {reps1} pass(es) in {elapsed1:.1f} s"}
     parity = {"rows": int(len(rows)), "worst": worst, "ok": bool(ok),
               "tolerance": "1e-5 row-relative" if spec.dtype == "f32" else "1e-2 absolute"}
     return base, parity
@@ -643,7 +669,9 @@ def main():
         result["roofline"]["unique_GBps"] = round(ub / (attn_avg * 1e-3) / 1e9, 2)
     torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        base, parity = cpu_baseline(spec, host_bits(out, spec.dtype), args.cpu_seconds)
+        # a one-thread time too for the decode workloads (every row one query token)
+        base, parity = cpu_baseline(spec, host_bits(out, spec.dtype), args.cpu_seconds,
+                                    one_thread=bool((spec.q_lens == 1).all()))
         result["cpu_baseline"] = base
         result["parity_sample"] = parity
     print(json.dumps(result), flush=True)

@@ -100,17 +100,21 @@ def attention(run: GpuRun, out=None, shared_prefixes=None):
 def compare(got_f64: np.ndarray, ref_f64: np.ndarray, dtype: str):
     """Tolerance check: fp32 per-row normwise relative <= 1e-5, fp16/bf16 |diff| <= 1e-2.
 
-    Returns (ok, worst) where worst is the largest normalized error."""
+    Every row of ``ref_f64`` is compared: callers pass the sampled rows only, so a
+    NaN in the reference (the oracle's mark for a row it did not compute) is an
+    error here, and so is an empty comparison.  Returns (ok, worst) where worst
+    is the largest normalized error."""
     g = got_f64.reshape(-1, got_f64.shape[-1])
     r = ref_f64.reshape(-1, ref_f64.shape[-1])
-    keep = ~np.isnan(r).any(axis=1)
-    g, r = g[keep], r[keep]
+    assert g.shape == r.shape, f"compared shapes differ: {g.shape} against {r.shape}"
+    assert len(r) > 0, "nothing to compare"
+    assert not np.isnan(r).any(), f"{int(np.isnan(r).any(axis=1).sum())} reference rows are NaN"
     if not np.isfinite(g).all():
         return False, float("inf")
     if dtype == "f32":
         num = np.abs(g - r).max(axis=1)
         den = np.maximum(np.abs(r).max(axis=1), 1e-30)
-        worst = float((num / den).max()) if len(r) else 0.0
+        worst = float((num / den).max())
         return worst <= 1e-5, worst
-    worst = float(np.abs(g - r).max()) if len(r) else 0.0
+    worst = float(np.abs(g - r).max())
     return worst <= 1e-2, worst
