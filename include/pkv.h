@@ -199,6 +199,30 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_token
                                            int32_t max_seq_len, int32_t num_q_heads,
                                            int32_t head_dim);
 
+/*
+ * paged_attention for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid allocation.  Same
+ * arguments, kernels and results as pkv_paged_attention, without the workspace
+ * arguments: the workspace is a static device array of PKV_STATIC_WORKSPACE_BYTES
+ * inside the library, one per GPU, held from the library's load on that GPU until
+ * the process ends.  The call allocates nothing and frees nothing.
+ *   PKV_ERR_WORKSPACE if pkv_paged_attention_workspace_bytes() for these bounds
+ *   exceeds PKV_STATIC_WORKSPACE_BYTES (256 MiB: every workload of up to 256 rows
+ *   of 8,192 tokens at 32 query heads, or a mixed batch of 16 prefill chunks over
+ *   32,768-token contexts plus 128 decodes, fits).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU
+ * (on different streams, or from different threads) race and must not be issued;
+ * calls in one stream are ordered and safe.  The array keeps the last call's
+ * contents; nothing in it needs to start at zero.
+ */
+#define PKV_STATIC_WORKSPACE_BYTES ((size_t)256 << 20)
+int pkv_paged_attention_no_alloc(const pkv_cache_t* cache, int32_t layer, void* out,
+                                 const void* q, const int32_t* block_tables, int32_t bt_stride,
+                                 const int32_t* seq_lens, const int32_t* query_start_loc,
+                                 int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len,
+                                 int32_t max_seq_len, int32_t num_q_heads, float scale,
+                                 uint32_t flags, void* stream);
+
 /* ---- host block allocator (plain C, no GPU use) -------------------------- */
 /*
  * A pool of equal blocks handed out on demand: a sequence gets a new block

@@ -21,11 +21,13 @@ STATUS = {
     -6: "PKV_ERR_HIP",
 }
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+STATIC_WORKSPACE_BYTES = 256 << 20  # PKV_STATIC_WORKSPACE_BYTES
 
 # every symbol include/pkv.h declares
 EXPORTS = (
     "pkv_status_string", "pkv_pool_bytes", "pkv_kv_cache_write", "pkv_copy_blocks",
     "pkv_paged_attention", "pkv_contiguous_attention", "pkv_paged_attention_workspace_bytes",
+    "pkv_paged_attention_no_alloc",
     "pkv_ba_create",
     "pkv_ba_destroy", "pkv_ba_alloc", "pkv_ba_incref", "pkv_ba_decref", "pkv_ba_refcount",
     "pkv_ba_num_free", "pkv_ba_num_blocks", "pkv_blocks_for_tokens", "pkv_seq_append_slots",
@@ -78,6 +80,8 @@ def load() -> ctypes.CDLL:
         "pkv_contiguous_attention": (ctypes.c_int, [pcache, i32, P, P, P, P, P, i32, i32, i32, i32,
                                                     f32, P, sz, P]),
         "pkv_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "pkv_paged_attention_no_alloc": (ctypes.c_int, [pcache, i32, P, P, P, i32, P, P, i32, i32,
+                                                        i32, i32, i32, f32, ctypes.c_uint32, P]),
         "pkv_ba_create": (ctypes.c_int, [i32, i32, pi32, ctypes.POINTER(P)]),
         "pkv_ba_destroy": (None, [P]),
         "pkv_ba_alloc": (ctypes.c_int, [P, pi32]),

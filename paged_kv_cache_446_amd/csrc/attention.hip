@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "attn_common.h"
 #include "pkv_host.h"
 
@@ -895,4 +897,56 @@ extern "C" int pkv_contiguous_attention(const pkv_cache_t* cache, int32_t layer,
   return attention_impl(cache, layer, out, q, first_block, run > 0 ? run : 1, 1, seq_lens,
                         query_start_loc, num_seqs, num_q_tokens, 1, max_seq_len, num_q_heads,
                         scale, workspace, workspace_bytes, 0, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free paged_attention: the workspace is a static device array.
+// ---------------------------------------------------------------------------
+namespace pkv {
+
+// One copy per GPU the library runs on, held until the process ends.  In host
+// code the name stands in for the variable and is not a device address: host code
+// uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[PKV_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_addr[kMaxDevices];
+
+// Device address of the current GPU's scratch array, looked up on the first call
+// on that GPU and kept.
+static int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" int pkv_paged_attention_no_alloc(const pkv_cache_t* cache, int32_t layer, void* out,
+                                            const void* q, const int32_t* block_tables,
+                                            int32_t bt_stride, const int32_t* seq_lens,
+                                            const int32_t* query_start_loc, int32_t num_seqs,
+                                            int32_t num_q_tokens, int32_t max_q_len,
+                                            int32_t max_seq_len, int32_t num_q_heads, float scale,
+                                            uint32_t flags, void* stream) {
+  if (!cache) return PKV_ERR_INVALID_ARGUMENT;
+  // every section of the workspace is written by the call's own kernels before it is
+  // read (plan counts, work lists, the prefill queue, partials): nothing to clear
+  const size_t need = pkv_paged_attention_workspace_bytes(num_seqs, num_q_tokens, max_seq_len,
+                                                          num_q_heads, cache->head_dim);
+  if (need > PKV_STATIC_WORKSPACE_BYTES) return PKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != PKV_OK) return rc;
+  return attention_impl(cache, layer, out, q, block_tables, bt_stride, 0, seq_lens,
+                        query_start_loc, num_seqs, num_q_tokens, max_q_len, max_seq_len,
+                        num_q_heads, scale, ws, PKV_STATIC_WORKSPACE_BYTES, flags, stream);
 }

@@ -90,6 +90,24 @@ def paged_attention(cache: PagedCache, out, q, block_tables, seq_lens, query_sta
                "pkv_paged_attention")
 
 
+def paged_attention_no_alloc(cache: PagedCache, out, q, block_tables, seq_lens, query_start_loc, *,
+                             num_q_heads: int, max_q_len: int, max_seq_len: int, scale: float,
+                             layer: int = 0, shared_prefixes: bool = False, stream=None):
+    """paged_attention with the library's static per-GPU workspace (no allocation)."""
+    lib = _lib.load()
+    for t, dt in ((block_tables, torch.int32), (seq_lens, torch.int32), (query_start_loc, torch.int32)):
+        assert t.dtype == dt and t.is_contiguous() and t.is_cuda
+    assert q.is_contiguous() and out.is_contiguous()
+    S = seq_lens.numel()
+    Tq = q.numel() // (num_q_heads * cache.head_dim)
+    _lib.check(lib.pkv_paged_attention_no_alloc(ctypes.byref(cache.desc), layer, _ptr(out), _ptr(q),
+                                                _ptr(block_tables), block_tables.shape[-1],
+                                                _ptr(seq_lens), _ptr(query_start_loc), S, Tq,
+                                                max_q_len, max_seq_len, num_q_heads, float(scale),
+                                                1 if shared_prefixes else 0, _stream(stream)),
+               "pkv_paged_attention_no_alloc")
+
+
 def contiguous_attention(cache: PagedCache, out, q, first_block, seq_lens, query_start_loc, *,
                          num_q_heads: int, max_seq_len: int, scale: float, workspace, layer: int = 0,
                          stream=None):
