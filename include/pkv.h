@@ -90,13 +90,19 @@ size_t pkv_pool_bytes(const pkv_cache_t* cache);
  * kv_cache_write: append the K and V entries of new tokens to the cache.  Each
  * token processed in prefill or decode adds one entry ([devpress], prefill /
  * decode / KV cache section: the cache grows by one note per token).
- *   k_new, v_new   device, [num_tokens][num_kv_heads][head_dim], pool dtype
+ *   k_new, v_new   device, [num_tokens][num_kv_heads][head_dim], pool dtype;
+ *                  k_new 16-byte aligned, v_new aligned to its element (16-byte
+ *                  alignment lets runs of consecutive slots write whole 16-byte
+ *                  chunks of V)
  *   slot_mapping   device int64 [num_tokens]; token i goes to block
- *                  slot/16, position slot%16; a negative slot is skipped
+ *                  slot/16, position slot%16; a negative slot, or one at or past
+ *                  num_blocks * 16, is skipped
  *   layer          which layer of the pools to write
- * Bytes are copied unchanged (no arithmetic).  Two tokens of one call must not
- * share a slot (the allocator never hands out a slot twice).  num_tokens = 0
- * is a no-op.
+ * Bytes are copied unchanged (no arithmetic); bytes of slots the call does not
+ * name keep their values.  Two tokens of one call must not share a slot (the
+ * allocator never hands out a slot twice).  num_tokens = 0 is a no-op; above
+ * 2^30 tokens, or with more than 65535 KV heads, the call returns
+ * PKV_ERR_UNSUPPORTED (split the write).
  */
 int pkv_kv_cache_write(const pkv_cache_t* cache, int32_t layer, const void* k_new,
                        const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
@@ -106,15 +112,17 @@ int pkv_kv_cache_write(const pkv_cache_t* cache, int32_t layer, const void* k_ne
  * copy_blocks: copy-on-write copies.  A sequence about to modify a shared
  * block first gets a copy and modifies that; the original block is left
  * unchanged ([blog], copy-on-write section).
- *   pairs   device int32 [num_pairs][2] = (src, dst) physical block ids
+ *   pairs   device int32 [num_pairs][2] = (src, dst) physical block ids; a pair
+ *           naming a block outside [0, num_blocks) is skipped
  * Copies K and V, every KV head and every layer, bit for bit.  A dst must not
  * appear twice, nor also as a src, in one call.  num_pairs = 0 is a no-op.
  */
 int pkv_copy_blocks(const pkv_cache_t* cache, const int32_t* pairs, int32_t num_pairs,
                     void* stream);
 
+/* ---- measurement only (not part of the hot path) -------------------------- */
 /*
- * Measurement only, not part of the attention path: read `bytes` of device
+ * Read `bytes` of device
  * memory at buf once, as a plain stream (16-byte non-temporal loads, several in
  * flight per thread), on `stream`.  The time it takes is the practical HBM read
  * rate the attention kernels are compared with, beside the nominal peak.
@@ -371,6 +379,39 @@ int32_t pkv_ba_num_cached(const pkv_ba_t* ba);
  * share after a fork or a prefix-cache hit ([devpress] "how memory is shared").
  * -1 for a NULL handle. */
 int32_t pkv_ba_num_shared(const pkv_ba_t* ba);
+
+/* ---- host checks of kernel metadata (plain C, no GPU use) ---------------- */
+/*
+ * The kernels trust the metadata they are given (they only skip slots and block
+ * ids outside the pool).  These calls check the rules of the block scheme on
+ * HOST copies of that metadata, for callers that want a check before a launch
+ * (tests, debugging).  Each returns PKV_OK, or PKV_ERR_INVALID_ARGUMENT and
+ * writes the index of the first offending entry to *bad (-1 when the sizes or
+ * pointers themselves are wrong); bad may be NULL.  Nothing is modified.
+ *
+ * pkv_check_slot_mapping: for kv_cache_write.  Every slot is negative (a
+ *   padding token) or below num_blocks * 16, and no slot is named twice: a
+ *   slot holds one token ([devpress] prefill / decode / KV cache section).
+ *   *bad is the earliest token with a slot out of the pool or a slot that an
+ *   earlier token already names.
+ */
+int pkv_check_slot_mapping(const int64_t* slots, int32_t num_tokens, int32_t num_blocks,
+                           int32_t* bad);
+/* pkv_check_copy_pairs: for copy_blocks.  pairs [num_pairs][2] = (src, dst):
+ *   both in [0, num_blocks), src != dst, no dst named twice, and no dst that is
+ *   also a src of the call (a copy goes to a new private block, [blog]
+ *   copy-on-write section).  *bad is the earliest pair that breaks a rule. */
+int pkv_check_copy_pairs(const int32_t* pairs, int32_t num_pairs, int32_t num_blocks,
+                         int32_t* bad);
+/* pkv_check_batch: for paged_attention, the preconditions it states: per
+ *   sequence 1 <= q_len <= max_q_len, 0 <= seq_len <= max_seq_len, q_len <=
+ *   seq_len unless seq_len = 0, ceil(seq_len / 16) <= bt_stride and each of those
+ *   table entries in [0, num_blocks); query_start_loc[0] >= 0 and
+ *   query_start_loc[num_seqs] <= num_q_tokens (else *bad = -1).  *bad is the
+ *   earliest sequence that breaks a rule. */
+int pkv_check_batch(const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_q_tokens,
+                    int32_t max_q_len, int32_t max_seq_len, int32_t num_blocks, int32_t* bad);
 
 #ifdef __cplusplus
 }

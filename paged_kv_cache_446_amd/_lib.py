@@ -34,6 +34,7 @@ EXPORTS = (
     "pkv_batch_append_slots", "pkv_seq_make_writable", "pkv_seq_fork", "pkv_seq_free",
     "pkv_prefix_hash", "pkv_seq_cache_lookup", "pkv_seq_cache_seal", "pkv_ba_num_cached",
     "pkv_ba_num_shared", "pkv_seq_reorder", "pkv_calib_stream_read",
+    "pkv_check_slot_mapping", "pkv_check_copy_pairs", "pkv_check_batch",
 )
 
 
@@ -104,6 +105,9 @@ def load() -> ctypes.CDLL:
         "pkv_ba_num_shared": (i32, [P]),
         "pkv_seq_reorder": (ctypes.c_int, [P, pi32, i32, pi32, pi32, i32, pi32, pi32]),
         "pkv_calib_stream_read": (ctypes.c_int, [P, sz, P, P]),
+        "pkv_check_slot_mapping": (ctypes.c_int, [pi64, i32, i32, pi32]),
+        "pkv_check_copy_pairs": (ctypes.c_int, [pi32, i32, i32, pi32]),
+        "pkv_check_batch": (ctypes.c_int, [pi32, i32, pi32, pi32, i32, i32, i32, i32, i32, pi32]),
     }
     for name in EXPORTS:
         fn = getattr(lib, name)

@@ -6,12 +6,16 @@ raw-bit views (int16 / int32) together with an explicit ``dtype``.
 """
 
 import ctypes
+import os
 
 import torch
 
-from . import _lib
+from . import _lib, checks
 
 _lib.load()  # no fallback: importing the binding without the HIP library fails here
+
+# PKV_DEBUG=1: copy each launch's metadata to the host and check it first (slow; synchronizes)
+DEBUG = os.environ.get("PKV_DEBUG", "0") not in ("", "0")
 
 _TORCH_DTYPES = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 
@@ -53,6 +57,8 @@ def kv_cache_write(cache: PagedCache, k_new, v_new, slot_mapping, layer: int = 0
     assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
     assert k_new.is_contiguous() and v_new.is_contiguous()
     T = slot_mapping.numel()
+    if DEBUG:
+        checks.slot_mapping(slot_mapping.cpu().numpy(), cache.num_blocks)
     _lib.check(lib.pkv_kv_cache_write(ctypes.byref(cache.desc), layer, _ptr(k_new), _ptr(v_new),
                                       _ptr(slot_mapping), T, _stream(stream)), "pkv_kv_cache_write")
 
@@ -61,6 +67,8 @@ def copy_blocks(cache: PagedCache, pairs, stream=None):
     lib = _lib.load()
     assert pairs.dtype == torch.int32 and pairs.is_contiguous()
     n = pairs.numel() // 2
+    if DEBUG:
+        checks.copy_pairs(pairs.cpu().numpy(), cache.num_blocks)
     _lib.check(lib.pkv_copy_blocks(ctypes.byref(cache.desc), _ptr(pairs) if n else None, n,
                                    _stream(stream)), "pkv_copy_blocks")
 
@@ -81,6 +89,9 @@ def paged_attention(cache: PagedCache, out, q, block_tables, seq_lens, query_sta
     assert q.is_contiguous() and out.is_contiguous()
     S = seq_lens.numel()
     Tq = q.numel() // (num_q_heads * cache.head_dim)
+    if DEBUG:
+        checks.batch(block_tables.cpu().numpy(), seq_lens.cpu().numpy(), query_start_loc.cpu().numpy(),
+                     Tq, max_q_len, max_seq_len, cache.num_blocks)
     _lib.check(lib.pkv_paged_attention(ctypes.byref(cache.desc), layer, _ptr(out), _ptr(q),
                                        _ptr(block_tables), block_tables.shape[-1], _ptr(seq_lens),
                                        _ptr(query_start_loc), S, Tq, max_q_len, max_seq_len,
@@ -100,6 +111,9 @@ def paged_attention_no_alloc(cache: PagedCache, out, q, block_tables, seq_lens, 
     assert q.is_contiguous() and out.is_contiguous()
     S = seq_lens.numel()
     Tq = q.numel() // (num_q_heads * cache.head_dim)
+    if DEBUG:
+        checks.batch(block_tables.cpu().numpy(), seq_lens.cpu().numpy(), query_start_loc.cpu().numpy(),
+                     Tq, max_q_len, max_seq_len, cache.num_blocks)
     _lib.check(lib.pkv_paged_attention_no_alloc(ctypes.byref(cache.desc), layer, _ptr(out), _ptr(q),
                                                 _ptr(block_tables), block_tables.shape[-1],
                                                 _ptr(seq_lens), _ptr(query_start_loc), S, Tq,

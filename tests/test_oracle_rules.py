@@ -239,6 +239,17 @@ def test_p6_negative_slot_is_skipped():
     assert int((kp != 0x7FC0).sum()) == 32 and int((kp[0, 1] == 0x3F80).sum()) == 32
 
 
+def test_p6_slot_past_the_pool_and_foreign_pairs_are_skipped():
+    kp = cache_ops.new_pool(1, 2, 1, 32, np.uint16, 0x7FC0)
+    vp = kp.copy()
+    k = np.full((3, 1, 32), 0x3F80, np.uint16)
+    cache_ops.kv_cache_write(kp, vp, k, k, np.array([32, 1 << 40, 5]), "bf16")
+    assert int((kp != 0x7FC0).sum()) == 32 and int((vp[0, 0] == 0x3F80).sum()) == 32
+    k0, v0 = kp.copy(), vp.copy()
+    cache_ops.copy_blocks(kp, vp, np.array([[0, 2], [-1, 1], [5, 1], [0, -3]], np.int32))
+    assert np.array_equal(kp, k0) and np.array_equal(vp, v0)
+
+
 def test_p6_copy_blocks_leaves_source_and_others():
     rng = np.random.default_rng(3)
     kp = rng.integers(0, 1 << 16, size=(2, 6, 2, 16 * 32), dtype=np.uint16)
