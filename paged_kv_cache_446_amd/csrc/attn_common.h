@@ -28,7 +28,6 @@ __device__ __forceinline__ int xcd_unit(int id, int live) {
   return j < live ? j : -1;
 }
 
-typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
 
 template <class DT, int D>
 struct Geo {
@@ -38,14 +37,28 @@ struct Geo {
   static constexpr int kX = 16 / DT::kBytes;           // elements per 16-byte chunk
 };
 
+// The exponentials of a column use a reference max that may lag its running max
+// by up to 2^kMaxLag (weights <= 256, far from overflow in fp32 and in the 16-bit
+// weight types); (m, l, o) stay consistent with whatever reference they carry.
+constexpr float kMaxLag = 8.f;
+
 template <class DT, int D>
 struct WaveState {
   u32x4 q[Geo<DT, D>::kChunks];  // Q^T operand of this lane's column
   f32x4 acc[Geo<DT, D>::kN];     // O^T: lane 16g+c holds dims 16n+4g..16n+4g+3 of column c
-  float m;                       // running max of the column (log2 domain)
-  float l;                       // running sum of this lane's 4 tokens per block
+  float m;                       // reference max of the column (log2 domain)
+  float l;                       // running sum of this lane's 4 tokens per block (relative to m)
 };
 
+template <class DT, int D>
+__device__ __forceinline__ void init_state(WaveState<DT, D>& st) {
+#pragma unroll
+  for (int n = 0; n < Geo<DT, D>::kN; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// Q^T operand chunk kk of lane 16g + c: head dims (4kk+g)*x .. +x of the lane's column
 template <class DT, int D>
 __device__ __forceinline__ void load_q(WaveState<DT, D>& st, const typename DT::T* qrow, bool valid,
                                        int g) {
@@ -53,10 +66,7 @@ __device__ __forceinline__ void load_q(WaveState<DT, D>& st, const typename DT::
 #pragma unroll
   for (int kk = 0; kk < Geo<DT, D>::kChunks; ++kk)
     st.q[kk] = valid ? q4[kk * 4 + g] : u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int n = 0; n < Geo<DT, D>::kN; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
+  init_state(st);
 }
 
 // One (block, KV head) tile of K and of V into registers: chunk i*64 + lane of
@@ -78,6 +88,16 @@ __device__ __forceinline__ void load_tile(const typename DT::T* kt, const typena
       vr[i] = v4[i * kWave + lane];
     }
   }
+}
+
+// max over the four lanes c, c+16, c+32, c+48 of a column (row swaps, no LDS)
+__device__ __forceinline__ float col_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <class DT, int D>
@@ -113,18 +133,22 @@ __device__ __forceinline__ void attend_block(WaveState<DT, D>& st,
   float sv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) sv[i] = (t0 + i <= lim) ? s[i] * scale_log2 : -INFINITY;
-  float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  bm = fmaxf(bm, shfl_xor(bm, 16));
-  bm = fmaxf(bm, shfl_xor(bm, 32));
-  const float mn = fmaxf(st.m, bm);
-  const float mu = (mn == -INFINITY) ? 0.f : mn;  // a column with nothing visible yet
-  const float alpha = fast_exp2(st.m - mu);
+  const float bm = col_max4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+  // st.m is the reference max of the exponentials: it moves (and the accumulators are
+  // rescaled) only when some column's block max exceeds it by more than 2^kMaxLag, a
+  // wave-wide decision; the first visible key of a column (st.m = -inf) always moves it
+  if (__builtin_amdgcn_ballot_w64(bm > st.m + kMaxLag)) {
+    const float mn = fmaxf(st.m, bm);
+    const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m - mn);
+#pragma unroll
+    for (int nn = 0; nn < Gm::kN; ++nn) st.acc[nn] *= alpha;
+    st.l *= alpha;
+    st.m = mn;
+  }
+  const float mu = st.m == -INFINITY ? 0.f : st.m;  // a column with nothing visible yet
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - mu);
-  st.m = mn;
-#pragma unroll
-  for (int nn = 0; nn < Gm::kN; ++nn) st.acc[nn] *= alpha;
 
   // slots at or past the sequence end may hold anything (even NaN): select, never multiply
   const bool tail = tok0 + kBlock > n;
@@ -140,22 +164,22 @@ __device__ __forceinline__ void attend_block(WaveState<DT, D>& st,
     // the sum uses the weights as P.V sees them, so the output is a convex
     // combination of V rows.  bf16 keeps 8 significant bits, too few for rows of a
     // few keys with large values: the weights enter P.V as hi + lo, the bf16 value
-    // and its bf16 rounding residue (hi + lo is exact in fp32, about 16 bits).
+    // and its bf16 rounding residue, which agree with the fp32 weights to about 16
+    // bits, so the sum takes the fp32 weights themselves.
     float ps;
     if constexpr (__is_same(DT, TBF16)) {
       const float h0 = bf16_bits_to_f32(pd0 & 0xffffu), h1 = bf16_bits_to_f32(pd0 >> 16);
       const float h2 = bf16_bits_to_f32(pd1 & 0xffffu), h3 = bf16_bits_to_f32(pd1 >> 16);
       pl0 = pack2_bf16(p[0] - h0, p[1] - h1);
       pl1 = pack2_bf16(p[2] - h2, p[3] - h3);
-      ps = ((h0 + bf16_bits_to_f32(pl0 & 0xffffu)) + (h1 + bf16_bits_to_f32(pl0 >> 16))) +
-           ((h2 + bf16_bits_to_f32(pl1 & 0xffffu)) + (h3 + bf16_bits_to_f32(pl1 >> 16)));
+      ps = (p[0] + p[1]) + (p[2] + p[3]);
     } else {
       ps = ((float)__builtin_bit_cast(_Float16, (uint16_t)(pd0 & 0xffffu)) +
             (float)__builtin_bit_cast(_Float16, (uint16_t)(pd0 >> 16))) +
            ((float)__builtin_bit_cast(_Float16, (uint16_t)(pd1 & 0xffffu)) +
             (float)__builtin_bit_cast(_Float16, (uint16_t)(pd1 >> 16)));
     }
-    st.l = st.l * alpha + ps;
+    st.l += ps;
     if (tail) {
       const uint32_t m0 = (t0 + 0 < n ? 0x0000ffffu : 0u) | (t0 + 1 < n ? 0xffff0000u : 0u);
       const uint32_t m1 = (t0 + 2 < n ? 0x0000ffffu : 0u) | (t0 + 3 < n ? 0xffff0000u : 0u);
@@ -177,7 +201,7 @@ __device__ __forceinline__ void attend_block(WaveState<DT, D>& st,
       }
     }
   } else {
-    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
     if (tail) {
 #pragma unroll
       for (int i = 0; i < Gm::kChunks; ++i) {

@@ -28,6 +28,7 @@ typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 constexpr int kBlock = 16;  // tokens per KV block
 constexpr int kWave = 64;
 
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));  // the same 16 bytes as a vector
 struct alignas(16) u32x4 {
   uint32_t x, y, z, w;
 };

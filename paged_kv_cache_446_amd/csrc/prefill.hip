@@ -291,16 +291,6 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
   if (tid == 0) queue[2] = sm_merge;
 }
 
-// max over the four lanes c, c+16, c+32, c+48 of a column (row swaps, no LDS)
-__device__ __forceinline__ float col_max4(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t w = __float_as_uint(y);
-  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 template <class DT, int D, int G>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restrict__ out,

@@ -162,3 +162,20 @@ def test_c_batch_append_matches_per_sequence_calls():
         assert np.array_equal(t, tabs[s])
     assert np.array_equal(slots, np.concatenate(ref)) and len(pairs) == 0
     assert a.num_free() == b.num_free()
+
+
+def test_no_kernel_uses_scratch_memory():
+    """The build's per-kernel resource report: no kernel spills or keeps an array in
+    per-lane scratch memory (hidden memory traffic), and the 16-bit one-tile decode
+    kernels keep the three waves per SIMD they are sized for."""
+    import json
+
+    path = os.path.join(ROOT, "_build", "kernel_resources.json")
+    if not os.path.exists(path):
+        pytest.fail("no kernel resource report: run python -m paged_kv_cache_446_amd.build")
+    res = json.load(open(path))
+    assert len(res) > 50
+    for name, r in res.items():
+        assert r["ScratchSize"] == 0 and r["VGPRs Spill"] == 0, name
+    one_tile = [r for n, r in res.items() if re.search(r"decode_kernelINS_5TBF16ELi128ELi\dELi1E", n)]
+    assert one_tile and all(r["Occupancy"] >= 3 for r in one_tile)
