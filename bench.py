@@ -396,6 +396,10 @@ def main():
                     help="decode workloads c2/c3 only: a batch of this many rows drawn from the "
                          "same length distribution (its own seed stream); default: the "
                          "workload's own batch")
+    ap.add_argument("--prefix-len", type=int, default=None,
+                    help="c4 only: shared prefix length (default 10000, a whole number of blocks: "
+                         "the step copies the last shared block explicitly; 9992 leaves that "
+                         "block partial, so the first private append copies it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--placement", default="random", choices=["random", "contiguous"],
@@ -435,6 +439,10 @@ def main():
         if args.config not in ("c2", "c3") or args.num_seqs < 1:
             raise SystemExit("--num-seqs applies to the decode workloads c2 and c3 (>= 1 rows)")
         spec = workloads.scaled_spec(args.config, num_seqs=args.num_seqs, variant=11)
+    elif args.prefix_len is not None:
+        if args.config != "c4" or not 1 <= args.prefix_len <= 65536:
+            raise SystemExit("--prefix-len applies to c4 (1 .. 65536 tokens)")
+        spec = workloads.scaled_spec("c4", prefix=args.prefix_len)
     else:
         spec = workloads.named_spec(args.config)
     log(f"workload {args.config}: S={spec.num_seqs} context tokens={int(spec.seq_lens.sum())} "
@@ -620,7 +628,8 @@ def main():
         "config": {
             "workload": WORKLOAD_NAMES[args.config] + (
                 "" if args.num_seqs is None else
-                f" (batch of {args.num_seqs} rows from the same length distribution)"),
+                f" (batch of {args.num_seqs} rows from the same length distribution)") + (
+                "" if args.prefix_len is None else f" (shared prefix of {args.prefix_len} tokens)"),
             "num_seqs": S,
             "query_tokens": spec.num_q_tokens,
             "context_tokens": int(spec.seq_lens.sum()),

@@ -509,6 +509,51 @@ def test_prefix_cache_reuse_gives_the_same_attention(prefix, tail_a, tail_b, q_b
     assert ok, worst
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_cache_stream_attends_over_its_own_prefix(seed):
+    """Recombined prompts on a small evicting pool, every token's K/V derived from its
+    whole prefix: each request's attention, from the C allocator's blocks, the cache
+    write and the attention kernels, matches the oracle over the request's own prompt.
+    A hit on a block computed under another prefix would move the output far outside
+    rounding (the same stream on the CPU catches a planted stale-child hit)."""
+    import torch
+
+    from paged_kv_cache_446_amd import ops
+    from paged_kv_cache_446_amd.allocator import BlockAllocator
+    from tests import prefix_stream as ps
+
+    gp = _gp()
+    gp.log(f"[prefix-stream] seed {seed}")
+    blocks = 14
+    order = np.random.default_rng(seed + 7).permutation(blocks).astype(np.int32)
+    alloc = BlockAllocator(blocks, free_order=order)
+    kp = torch.zeros(blocks * ps.HKV * 16 * ps.D, dtype=torch.int16, device="cuda:0")
+    vp = torch.zeros_like(kp)
+    cache = ops.PagedCache(kp, vp, ps.HKV, ps.D, dtype="bf16")
+    ws = torch.empty(ops.workspace_bytes(1, 1, 16 * 12, ps.HQ, ps.D), dtype=torch.uint8, device="cuda:0")
+
+    def write(slots, k, v):
+        ops.kv_cache_write(cache, gp.dev_bits(k, "bf16"), gp.dev_bits(v, "bf16"),
+                           torch.from_numpy(np.ascontiguousarray(slots)).to("cuda:0"))
+
+    def attend(t, nb, n, q):
+        qd = gp.dev_bits(q, "bf16")
+        out = torch.zeros_like(qd)
+        ops.paged_attention(cache, out, qd, torch.from_numpy(t[None, :nb].copy()).to("cuda:0"),
+                            torch.tensor([n], dtype=torch.int32, device="cuda:0"),
+                            torch.tensor([0, 1], dtype=torch.int32, device="cuda:0"),
+                            num_q_heads=ps.HQ, max_q_len=1, max_seq_len=n, scale=ps.SCALE,
+                            workspace=ws, shared_prefixes=alloc.num_shared() > 0)
+        torch.cuda.synchronize()
+        return numerics.to_f64(gp.host_bits(out, "bf16"), "bf16").reshape(q.shape)
+
+    hits, worst = ps.run(seed, alloc, write, attend)
+    gp.log(f"[prefix-stream] seed {seed}: {len(hits)} requests, {sum(h > 0 for h in hits)} with hits, "
+           f"worst {worst:.3g}")
+    assert sum(h > 0 for h in hits) > 10 and max(hits) >= 2
+    assert worst <= 1e-2
+
+
 @pytest.mark.parametrize("name,kw", [("c1", {}), ("c5", dict(num_seqs=12, max_len=1500, variant=3)),
                                      ("c4", dict(num_seqs=6, max_len=60, variant=3, prefix=37))])
 def test_step_captured_in_a_graph_replays_like_eager(name, kw):

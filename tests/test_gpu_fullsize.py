@@ -26,16 +26,29 @@ def _sample(spec, k=8):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c4-9992"])
 def test_full_size_sampled_rows_match_oracle(name):
+    """c4-9992: the 64 samples share a 9,992-token prefix, so its last block is
+    partial and shared; the first private append of each sample copies it."""
     import torch
 
     from tests import gpu_pipeline as gp
 
-    spec = workloads.named_spec(name)
+    if name == "c4-9992":
+        spec = workloads.scaled_spec("c4", prefix=9992)
+    else:
+        spec = workloads.named_spec(name)
     gp.log(f"[full] {name}: S={spec.num_seqs} context={int(spec.seq_lens.sum())} "
            f"max_q={int(spec.q_lens.max())} pool={spec.num_blocks}")
     run = gp.prepare(spec)
+    if name == "c4-9992":  # every sample copied the shared partial block before its first write
+        pairs = np.concatenate([ph.pairs for ph in run.flow.phases if len(ph.pairs)])
+        shared_last = 9992 // 16
+        assert len(pairs) >= spec.num_seqs - 1
+        assert len(set(pairs[:, 0].tolist())) == 1 and len(set(pairs[:, 1].tolist())) == len(pairs)
+        # afterwards each sample owns its own copy of that block; one kept the original
+        last = [int(t[shared_last]) for t in run.flow.tables]
+        assert len(set(last)) == spec.num_seqs and last.count(int(pairs[0, 0])) == 1
     bits = run.out_bits().copy()
     got = numerics.to_f64(bits, spec.dtype).reshape(spec.num_q_tokens, spec.num_q_heads, spec.head_dim)
 

@@ -369,3 +369,46 @@ def test_recombined_streams_catch_a_stale_child_hit():
         except AssertionError:
             caught += 1
     assert caught >= 5
+
+
+def _oracle_pool_stream(seed, alloc, blocks):
+    """The prefix-derived K/V stream on the oracle's pool image: writes and attention
+    through the oracle, blocks from ``alloc``."""
+    from oracle import attention as oattn
+    from oracle import cache_ops, numerics
+    from tests import prefix_stream as ps
+
+    kp = cache_ops.new_pool(1, blocks, ps.HKV, ps.D, np.uint16, 0x7FC0)
+    vp = kp.copy()
+
+    def write(slots, k, v):
+        cache_ops.kv_cache_write(kp, vp, k, v, slots, "bf16")
+
+    def attend(t, nb, n, q):
+        K, V = oattn.gather(kp, vp, t, n, "bf16")
+        return oattn.attend(numerics.to_f64(q, "bf16"), K, V, ps.SCALE)
+
+    return ps.run(seed, alloc, write, attend)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_derived_kv_stream_is_exact_with_model_and_c(seed):
+    """Each request attends over exactly its own prompt's K/V (the oracle's pool image,
+    so any deviation is a wrong block), with the model and with the C allocator."""
+    blocks = 14
+    order = np.random.default_rng(seed + 7).permutation(blocks).astype(np.int32)
+    for alloc in (oalloc.BlockAllocatorModel(blocks, free_order=order), _new_c(blocks, order)):
+        hits, worst = _oracle_pool_stream(seed, alloc, blocks)
+        assert worst == 0.0
+        assert sum(h > 0 for h in hits) > 10 and max(hits) >= 2
+
+
+def test_prefix_derived_kv_stream_sees_a_stale_child_hit():
+    # with the planted per-block-id keying, some request reads a block computed under
+    # another prefix, and its attention output moves far outside rounding
+    worst = []
+    for seed in (0, 1, 2):
+        blocks = 14
+        order = np.random.default_rng(seed + 7).permutation(blocks).astype(np.int32)
+        worst.append(_oracle_pool_stream(seed, _KeyedByParentBlock(blocks, free_order=order), blocks)[1])
+    assert max(worst) > 0.05, worst

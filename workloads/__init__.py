@@ -14,6 +14,7 @@ from .generate import (  # noqa: F401
     scaled_spec,
     verify_spec,
     normal_bits,
+    prefix_kv_bits,
     CONFIG_NAMES,
     run_flow,
     Flow,

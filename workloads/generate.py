@@ -56,6 +56,25 @@ def normal_bits(key, shape, dtype: str) -> np.ndarray:
     return _to_bits(rng.standard_normal(shape, dtype=np.float32), dtype)
 
 
+def prefix_kv_bits(tokens, num_kv_heads: int, head_dim: int, dtype: str):
+    """K and V bits [n][Hkv][D] of a prompt whose token t's entries depend on the whole
+    prefix tokens[0..t]: each token's N(0,1) draw is seeded by a running 64-bit BLAKE2b
+    digest of the token ids so far.  Two prompts get equal entries at a position exactly
+    when their prefixes up to it are equal, so a block reused under another prefix holds
+    different values."""
+    import hashlib
+
+    h = hashlib.blake2b(digest_size=8)
+    k = np.empty((len(tokens), num_kv_heads, head_dim), np.float32)
+    v = np.empty_like(k)
+    for t, tok in enumerate(np.asarray(tokens, dtype=np.int64)):
+        h.update(int(tok).to_bytes(8, "little", signed=True))
+        rng = np.random.default_rng(int.from_bytes(h.copy().digest(), "little"))
+        kv = rng.standard_normal((2, num_kv_heads, head_dim), dtype=np.float32)
+        k[t], v[t] = kv[0], kv[1]
+    return _to_bits(k, dtype), _to_bits(v, dtype)
+
+
 @dataclass
 class Spec:
     """One batch: per-sequence cached context and tokens appended this step."""
