@@ -91,15 +91,15 @@ size_t pkv_pool_bytes(const pkv_cache_t* cache);
  * token processed in prefill or decode adds one entry ([devpress], prefill /
  * decode / KV cache section: the cache grows by one note per token).
  *   k_new, v_new   device, [num_tokens][num_kv_heads][head_dim], pool dtype;
- *                  k_new 16-byte aligned, v_new aligned to its element (16-byte
- *                  alignment lets runs of consecutive slots write whole 16-byte
- *                  chunks of V)
+ *                  k_new 16-byte aligned, v_new aligned to its element
  *   slot_mapping   device int64 [num_tokens]; token i goes to block
  *                  slot/16, position slot%16; a negative slot, or one at or past
  *                  num_blocks * 16, is skipped
  *   layer          which layer of the pools to write
  * Bytes are copied unchanged (no arithmetic); bytes of slots the call does not
- * name keep their values.  Two tokens of one call must not share a slot (the
+ * name keep their values.  Four consecutive tokens that fill positions 4g..4g+3
+ * of one block (the tokens of a prefill chunk) have their V written as whole
+ * 16-byte chunks; other tokens' V is written element by element.  Two tokens of one call must not share a slot (the
  * allocator never hands out a slot twice).  num_tokens = 0 is a no-op; above
  * 2^30 tokens, or with more than 65535 KV heads, the call returns
  * PKV_ERR_UNSUPPORTED (split the write).

@@ -14,138 +14,144 @@
 
 namespace pkv {
 
-// grid (window of `win` consecutive tokens of the call, KV head); `win` is 1 to 16, chosen
-// on the host so that the grid fills the GPU (single decode tokens: one token per
-// workgroup; prefill chunks: 16).  A workgroup issues every load it needs at once (the
-// slots of its tokens and of three on either side, its tokens' K chunks, the V rows of
-// its tokens and of the three after them), then stores.
+// One workgroup per token, all KV heads.  Its loads do not wait for its slot: the
+// token's K chunks and V elements are read at once, beside the slots of the token and of
+// three neighbours on either side (scalar loads), so a decode token costs one memory
+// round trip before its stores.
+// Groups: when four consecutive tokens of the call hold positions 4g..4g+3 of one block
+// (what the tokens of a prefill chunk form), the group's first token writes the whole
+// group and the other three write nothing.  Its stores fill whole lines of the tiles:
 //   K: every 16-byte run of head dims stays contiguous in the tile (chunk (d/x) of token t
-//   sits at ((d/x)*16 + t)*x), so a token's K is 16-byte stores.
+//   sits at ((d/x)*16 + t)*x), so positions 4g..4g+3 of one chunk run are 64 contiguous
+//   bytes;
 //   V: four consecutive tokens of a dim are adjacent in the tile (a 16-byte chunk holds
-//   tokens 4g..4g+3 of x4 dims).  When the call writes all four positions 4g..4g+3 of a
-//   block through four consecutive tokens (a group: what the tokens of a prefill chunk
-//   form), the workgroup holding the group's first token writes each of its chunks as one
-//   16-byte store: whole lines of the tile.  A token outside such a group (a single decode
-//   token, the ragged ends of a chunk) is written element by element, so the other tokens
-//   of its chunks keep their bytes.  All tokens take that path when v_new is not 16-byte
-//   aligned (stage == 0).
+//   tokens 4g..4g+3 of x4 dims), so each chunk is one 16-byte store, gathered from the
+//   four tokens' elements.
+// A token outside such a group (a single decode token, the ragged ends of a chunk)
+// writes its own K chunks and its V element by element, so the other tokens of its V
+// chunks keep their bytes.
 // Slots at or past the pool's end (num_blocks * 16) are skipped like negative ones.
-constexpr int kWinMax = 16;                 // tokens per window, at most
-constexpr int kAround = 3;                  // neighbours on each side a group check may need
-constexpr int kRowsMax = kWinMax + kAround;  // V rows staged: the window and the three after it
-constexpr int kKPer = 4;    // K chunks per thread: 16 tokens x (D * e / 16 <= 64) / 256
-constexpr int kVPer = 5;    // V chunks staged per thread: 19 rows x (<= 64) / 256
+constexpr int kKPer = 2;  // K chunks per thread and pass (512 per pass: 8 heads of 256 bf16 dims)
+constexpr int kEPer = 8;  // V elements per thread and pass (2048 per pass)
 
 template <int kBytes>
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const u32x4* __restrict__ k_new, const void* __restrict__ v_new,
     const int64_t* __restrict__ slots, int num_tokens, u32x4* __restrict__ k_pool,
     void* __restrict__ v_pool, int num_kv_heads, int head_dim, int64_t layer_elems,
-    int64_t pool_slots, int stage, int win) {
+    int64_t pool_slots) {
   typedef typename std::conditional<kBytes == 2, uint16_t, uint32_t>::type E;
   constexpr int x = 16 / kBytes;
   constexpr int x4 = x / 4;
-  __shared__ int64_t sm_slot[kAround + kWinMax + kAround];  // tokens T0-3 .. T0+win+2; -1: none
-  __shared__ int sm_grp[kWinMax];  // per window token: offset in its group, -1 none, -2 skipped
-  extern __shared__ u32x4 sm_v[];  // V rows of tokens T0 .. T0+win+2, head h
-  const int T0 = blockIdx.x * win, h = blockIdx.y, tid = threadIdx.x;
-  const int chunks = head_dim / x;  // 16-byte chunks per (token, head)
-  const int row = num_kv_heads * chunks;
-  const int rows = win + kAround;
-  // all loads first
-  if (tid < win + 2 * kAround) {
-    const int u = T0 - kAround + tid;
+  const int tok = blockIdx.x, tid = threadIdx.x;
+  const int chunks = head_dim / x;                  // 16-byte chunks per (token, head)
+  const int row = num_kv_heads * chunks;            // 16-byte chunks per token
+  const int relems = num_kv_heads * head_dim;       // elements per token
+  const E* vn = (const E*)v_new;
+  // the first pass of K chunks and V elements, before the slots are known (past the end
+  // of the row: its last entry again, never stored)
+  u32v4 kv[kKPer];
+#pragma unroll
+  for (int j = 0; j < kKPer; ++j)
+    kv[j] = *(const u32v4*)&k_new[(int64_t)tok * row + min(tid + 256 * j, row - 1)];
+  E ve[kEPer];
+#pragma unroll
+  for (int j = 0; j < kEPer; ++j) ve[j] = vn[(int64_t)tok * relems + min(tid + 256 * j, relems - 1)];
+  // slots of tokens tok-3 .. tok+3 (-1: none, skipped or outside the pool)
+  int64_t sn[7];
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const int u = tok - 3 + j;
     const int64_t sl = (u >= 0 && u < num_tokens) ? slots[u] : -1;
-    sm_slot[tid] = (sl >= 0 && sl < pool_slots) ? sl : -1;
+    sn[j] = (sl >= 0 && sl < pool_slots) ? sl : -1;
   }
-  // loads of chunks past the end read the call's last chunk instead (always in bounds, so
-  // the loads need no branches and their registers stay registers); such values are
-  // never stored
-  const int64_t last_chunk = (int64_t)num_tokens * row - 1;
-  u32v4 kv[kKPer];  // vector types: these batches stay in registers
-#pragma unroll
-  for (int j = 0; j < kKPer; ++j) {  // K chunk i: token i % win, chunk i / win (tokens fastest)
-    const int i = tid + j * 256, k = i % win, ch = i / win;
-    const int64_t src = (int64_t)(T0 + k) * row + h * chunks + ch;
-    kv[j] = *(const u32v4*)&k_new[ch < chunks && T0 + k < num_tokens ? src : last_chunk];
-  }
-  if (stage) {
-    const u32x4* vn = (const u32x4*)v_new;
-    u32v4 vv[kVPer];
-#pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int i = tid + j * 256, k = i / chunks, ch = i - k * chunks;
-      const int64_t src = (int64_t)(T0 + k) * row + h * chunks + ch;
-      vv[j] = *(const u32v4*)&vn[k < rows && T0 + k < num_tokens ? src : last_chunk];
-    }
-#pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int i = tid + j * 256, k = i / chunks;
-      if (k < rows && T0 + k < num_tokens) *(u32v4*)&sm_v[i] = vv[j];
-    }
-  }
-  __syncthreads();
-  // group(k): for window token k, its offset r inside a group of four consecutive tokens
-  // holding positions 4g..4g+3 of one block, -1 when it is in no such group (always
-  // without staging), -2 when its slot is skipped
-  if (tid < win) {
-    const int64_t sl = sm_slot[kAround + tid];
-    int grp = -2;
-    if (sl >= 0) {
-      const int r = (int)(sl & 3);  // position % 4 (blocks hold 16 positions)
-      grp = stage ? r : -1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (sm_slot[kAround + tid - r + j] != sl - r + j) grp = -1;
-    }
-    sm_grp[tid] = grp;
-  }
+  const int64_t sl = sn[3];
+  if (sl < 0) return;
+  const int p = (int)(sl % kBlock);
   const int64_t tile = (int64_t)kBlock * head_dim;
-  auto tile_base = [&](int64_t sl) {  // first element of slot sl's (block, head h) tile
-    return layer_elems + ((sl / kBlock) * num_kv_heads + h) * tile;
-  };
+  const int64_t blk_base = layer_elems + (sl / kBlock) * num_kv_heads * tile;  // elements
+  // is the token in a group of four consecutive tokens holding positions 4g..4g+3?
+  const int r = p & 3;
+  bool grouped = true;
 #pragma unroll
-  for (int j = 0; j < kKPer; ++j) {
-    const int i = tid + j * 256, k = i % win, ch = i / win;
-    const int64_t sl = sm_slot[kAround + k];
-    if (ch < chunks && T0 + k < num_tokens && sl >= 0)
-      *(u32v4*)&k_pool[tile_base(sl) / x + (int64_t)ch * kBlock + sl % kBlock] = kv[j];
-  }
-  __syncthreads();
-  E* vdst = (E*)v_pool;
-  const E* sv = (const E*)sm_v;
-  // whole chunks of the groups that start in this window: chunk (m, c) of group g holds
-  // dims 16 (m x4 + r) + c, r < x4, of tokens 4g..4g+3
-  const int per_group = head_dim / x4;
-  for (int i = tid; i < win * per_group; i += blockDim.x) {
-    const int k = i / per_group, q = i - k * per_group;
-    if (sm_grp[k] != 0) continue;
-    const int64_t sl = sm_slot[kAround + k];
-    const int m = q >> 4, c = q & 15, g = (int)(sl % kBlock) >> 2;
-    // element r * 4 + j of the chunk: dim 16 (m x4 + r) + c of token k + j
-    uint32_t w[4];
+  for (int o = -3; o <= 3; ++o)  // token tok + o is the group's member o + r
+    if (o + r >= 0 && o + r <= 3) grouped = grouped && sn[3 + o] == sl + o;
+  E* vdst = (E*)v_pool + blk_base;
+  if (!grouped) {
+    // K: chunk i of the row is chunk ch = i % chunks of head i / chunks
+    for (int i0 = 0; i0 < row; i0 += 256 * kKPer) {
+      if (i0 > 0) {
 #pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      if constexpr (kBytes == 2) {
-        const int e0 = 2 * i2, e1 = 2 * i2 + 1;  // r = e / 4, j = e % 4
-        w[i2] = (uint32_t)sv[(k + e0 % 4) * head_dim + 16 * (m * x4 + e0 / 4) + c] |
-                ((uint32_t)sv[(k + e1 % 4) * head_dim + 16 * (m * x4 + e1 / 4) + c] << 16);
-      } else {
-        w[i2] = sv[(k + i2) * head_dim + 16 * m + c];
+        for (int j = 0; j < kKPer; ++j)
+          kv[j] = *(const u32v4*)&k_new[(int64_t)tok * row + min(i0 + tid + 256 * j, row - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < kKPer; ++j) {
+        const int i = i0 + tid + 256 * j;
+        if (i < row) {
+          const int h = i / chunks, ch = i - h * chunks;
+          *(u32v4*)&k_pool[(blk_base + h * tile) / x + (int64_t)ch * kBlock + p] = kv[j];
+        }
       }
     }
-    *(u32x4*)(vdst + tile_base(sl) + (((int64_t)m * 4 + g) * 16 + c) * x) = u32x4{w[0], w[1], w[2], w[3]};
-  }
-  // the other tokens, element by element
-  const E* vsrc = (const E*)v_new + ((int64_t)T0 * num_kv_heads + h) * head_dim;
-  for (int i = tid; i < win * head_dim; i += blockDim.x) {
-    const int k = i / head_dim, d = i - k * head_dim;
-    if (sm_grp[k] != -1) continue;
-    const int64_t sl = sm_slot[kAround + k];
-    const int p = (int)(sl % kBlock), g = p >> 2, j = p & 3;
-    const int n = d >> 4, c = d & 15, m = n / x4, r = n - m * x4;
-    const E val = stage ? sv[k * head_dim + d] : vsrc[(int64_t)k * num_kv_heads * head_dim + d];
-    vdst[tile_base(sl) + ((((int64_t)m * 4 + g) * 16 + c) * x4 + r) * 4 + j] = val;
+    // V element by element: element i is dim d = i % head_dim of head i / head_dim
+    const int g = p >> 2, jj = p & 3;
+    for (int i0 = 0; i0 < relems; i0 += 256 * kEPer) {
+      if (i0 > 0) {
+#pragma unroll
+        for (int j = 0; j < kEPer; ++j)
+          ve[j] = vn[(int64_t)tok * relems + min(i0 + tid + 256 * j, relems - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < kEPer; ++j) {
+        const int i = i0 + tid + 256 * j;
+        if (i < relems) {
+          const int h = i / head_dim, d = i - h * head_dim;
+          const int n = d >> 4, c = d & 15, m = n / x4, rr = n - m * x4;
+          vdst[h * tile + ((((int64_t)m * 4 + g) * 16 + c) * x4 + rr) * 4 + jj] = ve[j];
+        }
+      }
+    }
+  } else if (r == 0) {
+    // the group's first token writes the group.  K: entry i is token j = i % 4 of chunk
+    // i / 4 of the row, so four neighbouring lanes fill the 64 bytes of positions
+    // p .. p + 3 of one chunk run
+    for (int i0 = 0; i0 < 4 * row; i0 += 256 * kKPer) {
+      u32v4 kg[kKPer];
+#pragma unroll
+      for (int j = 0; j < kKPer; ++j) {
+        const int i = min(i0 + tid + 256 * j, 4 * row - 1);
+        kg[j] = *(const u32v4*)&k_new[(int64_t)(tok + (i & 3)) * row + (i >> 2)];
+      }
+#pragma unroll
+      for (int j = 0; j < kKPer; ++j) {
+        const int i = i0 + tid + 256 * j;
+        if (i < 4 * row) {
+          const int ci = i >> 2, h = ci / chunks, ch = ci - h * chunks;
+          *(u32v4*)&k_pool[(blk_base + h * tile) / x + (int64_t)ch * kBlock + p + (i & 3)] = kg[j];
+        }
+      }
+    }
+    // V: whole chunks.  Chunk (m, c) of head h holds dims 16 (m x4 + rr) + c, rr < x4, of
+    // the group's tokens j = 0..3, element rr * 4 + j
+    const int g = p >> 2;
+    const int per_head = head_dim / x4;  // chunks of one group in one head's tile
+    for (int i = tid; i < num_kv_heads * per_head; i += blockDim.x) {
+      const int h = i / per_head, q = i - h * per_head, m = q >> 4, c = q & 15;
+      const E* src = vn + (int64_t)tok * relems + h * head_dim + 16 * m * x4 + c;
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (kBytes == 2) {  // elements 2k and 2k+1: (rr, j) = (k / 2, 2 (k % 2)) and +1
+          const int rr = k >> 1, j0 = 2 * (k & 1);
+          w[k] = (uint32_t)src[(int64_t)j0 * relems + 16 * rr] |
+                 ((uint32_t)src[(int64_t)(j0 + 1) * relems + 16 * rr] << 16);
+        } else {
+          w[k] = src[(int64_t)k * relems];
+        }
+      }
+      *(u32v4*)&vdst[h * tile + (((int64_t)m * 4 + g) * 16 + c) * x] = u32v4{w[0], w[1], w[2], w[3]};
+    }
   }
 }
 
@@ -197,30 +203,20 @@ extern "C" int pkv_kv_cache_write(const pkv_cache_t* cache, int32_t layer, const
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARGUMENT;
   if (!aligned16(k_new) || ((uintptr_t)v_new % elem_bytes(cache->dtype))) return PKV_ERR_INVALID_ARGUMENT;
-  if (num_tokens > (1 << 30) || cache->num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;  // grid limits
+  if (num_tokens > (1 << 30)) return PKV_ERR_UNSUPPORTED;  // grid limit
   const int64_t layer_elems = (int64_t)layer * cache->num_blocks * cache->num_kv_heads *
                               kBlock * cache->head_dim;
   const int64_t pool_slots = (int64_t)cache->num_blocks * kBlock;
-  // window: the largest of 16, 8, 4, 2, 1 tokens that still gives 2048 workgroups (8 per
-  // CU), so that a few decode tokens spread over the GPU and a prefill chunk's groups stay
-  // in one workgroup
-  int win = kWinMax;
-  while (win > 1 && (int64_t)((num_tokens + win - 1) / win) * cache->num_kv_heads < 2048) win /= 2;
-  // LDS for one head's V rows of a window and the three tokens after it (at most 19 KiB);
-  // staged when v_new is 16-byte aligned
-  const int stage = aligned16(v_new);
-  const size_t lds =
-      stage ? (size_t)(win + kAround) * cache->head_dim * elem_bytes(cache->dtype) : 0;
   hipStream_t st = (hipStream_t)stream;
-  dim3 grid((num_tokens + win - 1) / win, cache->num_kv_heads), block(256);
+  dim3 grid(num_tokens), block(256);
   if (elem_bytes(cache->dtype) == 2)
-    hipLaunchKernelGGL(kv_cache_write_kernel<2>, grid, block, lds, st, (const u32x4*)k_new, v_new,
+    hipLaunchKernelGGL(kv_cache_write_kernel<2>, grid, block, 0, st, (const u32x4*)k_new, v_new,
                        slot_mapping, num_tokens, (u32x4*)cache->k_pool, cache->v_pool,
-                       cache->num_kv_heads, cache->head_dim, layer_elems, pool_slots, stage, win);
+                       cache->num_kv_heads, cache->head_dim, layer_elems, pool_slots);
   else
-    hipLaunchKernelGGL(kv_cache_write_kernel<4>, grid, block, lds, st, (const u32x4*)k_new, v_new,
+    hipLaunchKernelGGL(kv_cache_write_kernel<4>, grid, block, 0, st, (const u32x4*)k_new, v_new,
                        slot_mapping, num_tokens, (u32x4*)cache->k_pool, cache->v_pool,
-                       cache->num_kv_heads, cache->head_dim, layer_elems, pool_slots, stage, win);
+                       cache->num_kv_heads, cache->head_dim, layer_elems, pool_slots);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

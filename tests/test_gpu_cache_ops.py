@@ -127,9 +127,9 @@ def _run_slots(rng, nb, kind):
                                                  ("f16", 2, 64, True), ("f32", 4, 128, True),
                                                  ("f32", 8, 256, True), ("bf16", 1, 256, False)])
 def test_write_runs_bit_exact(kind, dtype, hkv, d, aligned):
-    """Runs of consecutive slots (whole 16-byte V chunks) next to partial chunks whose
-    other tokens were written before; v_new off 16-byte alignment and rows too large
-    to stage take the element-by-element path."""
+    """Runs of consecutive slots (groups of four written as whole K lines and V
+    chunks) next to ragged ends and single tokens written element by element, in
+    chunks whose other tokens were written before; v_new also off 16-byte alignment."""
     import torch
 
     from paged_kv_cache_446_amd import ops
