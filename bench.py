@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak, published
 
 WORKLOAD_NAMES = {
     "c1": "tiny paged decode: 4 seqs (1,17,33,50), 4 heads MHA, head_dim 64, fp32",
@@ -609,6 +610,60 @@ def main():
     log(f"cold-cache attention {cold_ms * 1e3:.1f} us (warm {attn_avg * 1e3:.1f}); "
         f"stream read {stream_gbs:.0f} GB/s")
 
+    # chunks past 32 (token, head) columns per KV head take the tiled prefill kernel, which
+    # is bound by MFMA, not HBM: timed alone over the same cache, for its own roofline
+    prefill = None
+    pf_rows = np.nonzero(spec.q_lens * spec.group > 32)[0]
+    if len(pf_rows) and args.kernel == "paged" and spec.dtype != "f32":
+        sel = torch.from_numpy(pf_rows.astype(np.int64)).to(dev)
+        pq_lens = spec.q_lens[pf_rows].astype(np.int64)
+        q_rows = np.concatenate([np.arange(spec.query_start_loc[s], spec.query_start_loc[s + 1])
+                                 for s in pf_rows])
+        p_tables = tables.index_select(0, sel).contiguous()
+        p_lens = seq_lens.index_select(0, sel).contiguous()
+        p_qsl = torch.from_numpy(np.concatenate([[0], np.cumsum(pq_lens)]).astype(np.int32)).to(dev)
+        p_q = q.view(spec.num_q_tokens, -1).index_select(0, torch.from_numpy(q_rows).to(dev)).contiguous()
+        p_out = torch.zeros_like(p_q)
+        p_max_n = int(spec.seq_lens[pf_rows].max())
+        p_ws = torch.empty(ops.workspace_bytes(len(pf_rows), len(q_rows), p_max_n, spec.num_q_heads,
+                                               spec.head_dim), dtype=torch.uint8, device=dev)
+
+        def prefill_call():
+            ops.paged_attention(cache, p_out, p_q, p_tables, p_lens, p_qsl,
+                                num_q_heads=spec.num_q_heads, max_q_len=int(pq_lens.max()),
+                                max_seq_len=p_max_n, scale=spec.scale, workspace=p_ws)
+
+        for _ in range(args.warmup):
+            prefill_call()
+        pev = []
+        for _ in range(K):
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record()
+            prefill_call()
+            eb.record()
+            pev.append((ea, eb))
+        torch.cuda.synchronize()
+        pf_ms = float(np.mean([a.elapsed_time(b) for a, b in pev]))
+        ctx = spec.seq_lens[pf_rows].astype(np.int64) - pq_lens
+        # masked (token, key) pairs not counted: row i of a chunk sees ctx + i + 1 keys
+        flops = int((4 * spec.num_q_heads * spec.head_dim *
+                     (pq_lens * ctx + pq_lens * (pq_lens + 1) // 2)).sum())
+        tflops = flops / (pf_ms * 1e-3) / 1e12
+        prefill = {
+            "kernel": "paged_attention over the batch's prefill chunks alone (prefill plan + "
+                      "tiled prefill kernel + merge)",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(pf_ms * 1e3, 2),
+            "chunks": int(len(pf_rows)),
+        }
+        log(f"prefill chunks alone: {pf_ms * 1e3:.1f} us, {tflops:.0f} TFLOP/s")
+
     kv_bytes, attn_bytes = algorithmic_bytes(spec)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = attn_bytes / (attn_avg * 1e-3) / 1e9
@@ -670,6 +725,13 @@ def main():
             "cold_cache_GBps": round(attn_bytes / (cold_ms * 1e-3) / 1e9, 2),
         },
     }
+    if prefill is not None and prefill["avg_launch_us"] > 0.5 * result["roofline"]["avg_launch_us"]:
+        # the prefill kernel dominates the call: the roofline is its MFMA one; the whole
+        # call's HBM figures stay beside it
+        result["roofline_call_hbm"] = result["roofline"]
+        result["roofline"] = prefill
+    elif prefill is not None:
+        result["roofline_prefill"] = prefill
     if args.placement == "random" and alloc.num_shared() > 0:
         # rows share blocks: the algorithmic bytes count a shared block once per row that
         # reads it; the distinct blocks are what HBM must deliver
