@@ -31,8 +31,8 @@ namespace pkv {
 // writes its own K chunks and its V element by element, so the other tokens of its V
 // chunks keep their bytes.
 // Slots at or past the pool's end (num_blocks * 16) are skipped like negative ones.
-constexpr int kKPer = 2;  // K chunks per thread and pass (512 per pass: 8 heads of 256 bf16 dims)
-constexpr int kEPer = 8;  // V elements per thread and pass (2048 per pass)
+constexpr int kKPer = 2;  // K chunks per thread and pass (512 per pass: 8 heads of 256 fp32 dims)
+constexpr int kEPer = 8;  // V elements per thread and pass (2048 per pass: 8 heads of 256 dims)
 
 template <int kBytes>
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
