@@ -108,8 +108,7 @@ __global__ __launch_bounds__(256) void prefill_wave_kernel(
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfBuckets = 64;     // context-length classes of the plan (1024 tokens each)
-constexpr int kPfDepth = 2;        // steps of K/V in flight per thread (register stages)
-constexpr int kPfTableMax = 8192;  // block-table entries an item keeps in LDS (131072 tokens)
+constexpr int kPfTableMax = 4096;  // block-table entries an item keeps in LDS (65536 tokens)
 // The exponentials use a reference max that may lag the true running max by
 // up to 2^kPfLag (weights <= 2^8, far from overflow); the accumulators are
 // rescaled only when some column's max moves further than that.
@@ -118,14 +117,16 @@ constexpr float kPfLag = 8.f;
 template <class DT, int D>
 struct PfGeo {
   static constexpr int kCT = D <= 128 ? 2 : 1;                      // 16-column tiles per wave
-  static constexpr int kSB = D <= 128 ? 4 : 2;                      // KV blocks per pipeline step
+  static constexpr int kSB = D <= 128 ? 4 : 2;                      // KV blocks per compute step
+  static constexpr int kSS = D <= 128 ? 2 : 1;                      // compute steps per LDS stage
+  static constexpr int kStageB = kSB * kSS;                         // KV blocks per LDS stage
   static constexpr int kCols = kPfWaves * kCT * 16;                 // columns per item
   static constexpr int kTileChunks = kBlock * D * DT::kBytes / 16;  // 16-byte chunks per tile
-  static constexpr int kStageChunks = 2 * kSB * kTileChunks;        // K and V of a step
+  static constexpr int kStageChunks = 2 * kStageB * kTileChunks;    // K and V of a stage
   static constexpr int kPerThread = kStageChunks / kPfThreads;
   static constexpr int kLdsBytes = 2 * kStageChunks * 16;           // double buffer
   static_assert(kStageChunks % kPfThreads == 0, "whole chunks per thread");
-  static_assert(kSB % 2 == 0 && kPfTableMax % kSB == 0, "whole block pairs per step");
+  static_assert(kSB % 2 == 0 && kPfTableMax % kStageB == 0, "whole block pairs per step");
   static_assert(kLdsBytes + kPfTableMax * 4 + 64 <= 160 * 1024, "LDS of one workgroup");
 };
 
@@ -305,9 +306,10 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
   typedef PfGeo<DT, D> P;
   constexpr int kCT = P::kCT;
   constexpr int kSB = P::kSB;
+  constexpr int kStageB = P::kStageB;
   constexpr int kTC = P::kTileChunks;
   constexpr int QT = P::kCols / G;  // query tokens per item
-  // LDS stage: [K of blocks 0..kSB-1][V of block pair 0: slices r=0][r=1][pair 1: r=0][r=1]...
+  // LDS stage: [K of blocks 0..kStageB-1][V of block pair 0: slices r=0][r=1][pair 1: ...]...
   // A V entry of 16 bytes holds the 8-byte half r of one chunk for the pair's first block,
   // then for its second: exactly one A operand of the 32-token V^T.P^T product.
   extern __shared__ u32x4 sm_stage[];
@@ -362,30 +364,34 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
     // boundary other than the last block falls on a whole step
     int seg0 = kb0;  // first block of the block-table segment held in sm_bt
 
-    // K/V of step j: registers -> LDS buffer j & 1; the next kPfDepth-1 steps are in flight.
-    // Thread chunk k of a step is chunk ci of tile t = 2b + (0 for K, 1 for V) of the step's
-    // block b.  Loads are unconditional (blocks past the visible range re-read the last one)
-    // so that each wait covers exactly one step; masking happens when the step is stored.
-    u32x4 stg[kPfDepth][P::kPerThread];
-    auto fetch_stage = [&](u32x4 (&dst)[P::kPerThread], int j) {
+    // K/V of stage j: registers -> LDS buffer j & 1, a compute step's blocks at a time: the
+    // part for compute step ss of stage j + 1 is loaded while step ss of stage j computes,
+    // then stored into the other buffer.  Thread chunk k of a stage is chunk ci of tile
+    // t = 2b + (0 for K, 1 for V) of the stage's block b; part ss holds chunks
+    // k = ss * kPH .. ss * kPH + kPH - 1, the tiles of blocks ss * kSB .. ss * kSB + kSB - 1.
+    // Loads are unconditional (blocks past the visible range re-read the last one) so that
+    // each wait covers exactly one part; masking happens when the part is stored.
+    constexpr int kPH = P::kPerThread / P::kSS;
+    u32x4 stg[kPH];
+    auto fetch_part = [&](int j, int ss) {
 #pragma unroll
-      for (int k = 0; k < P::kPerThread; ++k) {
-        const int idx = tid + k * kPfThreads;
+      for (int k = 0; k < kPH; ++k) {
+        const int idx = tid + (ss * kPH + k) * kPfThreads;
         const int t = idx / kTC, ci = idx % kTC;
-        const int blk = min(kSB * j + (t >> 1), kb1 - 1);
+        const int blk = min(kStageB * j + (t >> 1), kb1 - 1);
         const int64_t phys = sm_bt[blk - seg0];
         const u32x4* src = (const u32x4*)(((t & 1) ? vp : kp) + phys * blk_elems + head_off);
-        dst[k] = src[ci];
+        stg[k] = src[ci];
       }
     };
-    auto store_stage = [&](const u32x4 (&src)[P::kPerThread], int j, int buf) {
+    auto store_part = [&](int j, int ss, int buf) {
       u32x4* st = sm_stage + buf * P::kStageChunks;
 #pragma unroll
-      for (int k = 0; k < P::kPerThread; ++k) {
-        const int idx = tid + k * kPfThreads;
+      for (int k = 0; k < kPH; ++k) {
+        const int idx = tid + (ss * kPH + k) * kPfThreads;
         const int t = idx / kTC, ci = idx % kTC;
-        const int b = t >> 1, blk = kSB * j + b;
-        u32x4 v = blk < kb1 ? src[k] : u32x4{0, 0, 0, 0};
+        const int b = t >> 1, blk = kStageB * j + b;
+        u32x4 v = blk < kb1 ? stg[k] : u32x4{0, 0, 0, 0};
         if (t & 1) {
           if (blk * kBlock + kBlock > n) {
             // V of slots past the sequence end may be anything: zero it (tokens 4g'..4g'+3)
@@ -397,7 +403,7 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
             v.z &= m0;
             v.w &= m1;
           }
-          uint2* v2 = (uint2*)(st + (kSB + 2 * (b >> 1)) * kTC);
+          uint2* v2 = (uint2*)(st + (kStageB + 2 * (b >> 1)) * kTC);
           v2[2 * ci + (b & 1)] = uint2{v.x, v.y};
           v2[2 * (kTC + ci) + (b & 1)] = uint2{v.z, v.w};
         } else {
@@ -405,9 +411,11 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
         }
       }
     };
-    auto compute = [&](int j, int buf) {
-      const u32x4* st = sm_stage + buf * P::kStageChunks;
-      const int t0 = kSB * kBlock * j;
+    // compute step ss of stage j: the stage's blocks ss * kSB .. ss * kSB + kSB - 1
+    auto compute = [&](int j, int buf, int ss) {
+      const u32x4* st = sm_stage + buf * P::kStageChunks + ss * kSB * kTC;  // its K tiles
+      const u32x4* sv = sm_stage + buf * P::kStageChunks + (kStageB + ss * kSB) * kTC;  // V
+      const int t0 = (kStageB * j + kSB * ss) * kBlock;
       const bool need_mask = t0 + kSB * kBlock - 1 > wave_min_lim;
       // S^T = K.Q^T: lane 16g+c holds tokens 4g..4g+3 of each block for column c
       f32x4 sc[kSB][kCT];
@@ -483,8 +491,8 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
         // O^T += V^T . P^T over the pair's 32 tokens, and the row sums against a slice of ones
 #pragma unroll
         for (int mm = 0; mm < Gm::kChunks; ++mm) {
-          const u32x4 lo = st[(kSB + 2 * pp) * kTC + mm * kWave + lane];      // dim slice 2mm
-          const u32x4 hi = st[(kSB + 2 * pp + 1) * kTC + mm * kWave + lane];  // slice 2mm+1
+          const u32x4 lo = sv[(2 * pp) * kTC + mm * kWave + lane];      // dim slice 2mm
+          const u32x4 hi = sv[(2 * pp + 1) * kTC + mm * kWave + lane];  // slice 2mm+1
 #pragma unroll
           for (int ct = 0; ct < kCT; ++ct) {
             acc[ct][2 * mm] = mma_k32(lo, pk[ct], acc[ct][2 * mm], DT());
@@ -501,22 +509,22 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
       const int seg_n = min(kPfTableMax, kb1 - seg0);
       for (int i = tid; i < seg_n; i += kPfThreads) sm_bt[i] = btr[seg0 + i];
       __syncthreads();
-      const int js = seg0 / kSB, je = (seg0 + seg_n + kSB - 1) / kSB;
-      const int jl = je - 1;  // steps past the segment fetch its last step again (unused)
+      const int js = seg0 / kStageB, je = (seg0 + seg_n + kStageB - 1) / kStageB;
+      const int jl = je - 1;  // stages past the segment fetch its last stage again (unused)
 #pragma unroll
-      for (int u = 0; u + 1 < kPfDepth; ++u) fetch_stage(stg[u], min(js + u, jl));
-      store_stage(stg[0], js, js & 1);
+      for (int ss = 0; ss < P::kSS; ++ss) {
+        fetch_part(js, ss);
+        store_part(js, ss, js & 1);
+      }
       __syncthreads();
-      for (int j0 = js; j0 < je; j0 += kPfDepth) {
+      for (int j = js; j < je; ++j) {
 #pragma unroll
-        for (int u = 0; u < kPfDepth; ++u) {
-          const int j = j0 + u;  // K/V of step j: stg[u] and LDS buffer j & 1
-          if (j >= je) break;
-          fetch_stage(stg[(u + kPfDepth - 1) % kPfDepth], min(j + kPfDepth - 1, jl));
-          if (wave_active) compute(j, j & 1);
-          if (j + 1 < je) store_stage(stg[(u + 1) % kPfDepth], j + 1, (j + 1) & 1);
-          __syncthreads();
+        for (int ss = 0; ss < P::kSS; ++ss) {
+          fetch_part(min(j + 1, jl), ss);
+          if (wave_active) compute(j, j & 1, ss);
+          if (j + 1 < je) store_part(j + 1, ss, (j + 1) & 1);
         }
+        __syncthreads();
       }
     }
 #pragma unroll
@@ -638,7 +646,7 @@ static int tiled_launch(const AttnArgs& a) {
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.seq_lens, a.qsl,
                      a.num_seqs, a.num_kv_heads, G, P::kCols,
                      small_chunk_max_cols(DT::kBytes == 2 ? PKV_BF16 : PKV_F32, D), a.bt_stride,
-                     P::kSB, grid < kPfSplitWorkers ? grid : kPfSplitWorkers, (int)a.pf_slots,
+                     P::kStageB, grid < kPfSplitWorkers ? grid : kPfSplitWorkers, (int)a.pf_slots,
                      items, tiles, merges, queue, (int)(a.pf_items + a.pf_slots));
   hipLaunchKernelGGL((prefill_tiled_kernel<DT, D, G>), dim3(grid), dim3(kPfThreads), P::kLdsBytes,
                      a.stream, (const T*)a.q, (T*)a.out, (const T*)a.kp, (const T*)a.vp, a.bt,
