@@ -18,18 +18,18 @@
 // 16x16x16 matrix instructions for O^T += V^T . P^T, whose P^T operand is the
 // S^T result already in place.
 //
-// Decode splits the context of a sequence into partitions of kPartBlocks
-// blocks (1024 tokens).  Short chunks (a few query tokens, e.g. the k+1
-// tokens that verify a speculative draft) take the same kernel with their
+// Decode splits the context of a sequence into partitions of 1024, 2048, 3072 or
+// 4096 tokens, a size a plan kernel chooses per call from the lengths of the whole
+// batch (1024 when rows share blocks).  Short chunks (a few query tokens, e.g. the
+// k+1 tokens that verify a speculative draft) take the same kernel with their
 // q_len * G columns in one or two column tiles, so K/V are read once per row.
-// One workgroup per (sequence, partition, KV head):
-// its four wavefronts take every fourth block, streaming K/V tiles with
-// non-temporal loads (each tile is read once), merge through LDS, and a
-// second kernel merges the partitions of long sequences with the log-sum-exp
-// rule.  Work items are listed longest first and workgroup ids are remapped
-// so that every XCD takes its share of them in that order, with the KV heads
-// of one item together on one XCD (hardware dispatch deals consecutive
-// workgroups round-robin over the eight XCDs).
+// One workgroup per work unit (sequence, partition, KV head): its four wavefronts
+// take every fourth block, streaming K/V tiles with non-temporal loads (each tile
+// is read once), merge through LDS, and a second kernel merges the partitions of
+// long sequences with the log-sum-exp rule.  Work items are listed longest first
+// and dealt to the XCDs in rounds (hardware dispatch deals consecutive workgroups
+// round-robin over the eight XCDs), or partition-major when rows share blocks, so
+// that the rows reading one tile run together on one XCD.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
