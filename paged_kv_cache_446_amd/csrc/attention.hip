@@ -41,6 +41,7 @@
 namespace pkv {
 
 constexpr int kPartBlocks = 64;  // blocks of the shortest decode partition (1024 tokens)
+constexpr int kOddRounds = 10;   // dealing cycle: odd XCDs take 10 items per 11 of an even one
 constexpr int kPartChoices = 4;  // partitions of 1, 2, 3 or 4 x kPartBlocks blocks
 constexpr int kPartMax = kPartChoices * kPartBlocks;
 constexpr int kPlanLevels = 2048;  // partition indices the plan orders items by (2M tokens)
@@ -546,12 +547,20 @@ void decode_kernel(const typename DT::T* __restrict__ q, typename DT::T* __restr
         i = j % live;
         h = j / live;
       } else {
-        // longest first: the r-th unit of XCD x is KV head r % H of the item at position
-        // x of round r / H of the list, counted from the other end in odd rounds (so no
-        // XCD takes the longest item of every round).  Past the list: done.
+        // longest first: the r-th unit of XCD x is KV head r % H of the XCD's item r / H.
+        // The list is dealt in rounds of 8 items, item x of a round to XCD x, counted from
+        // the other end in odd rounds (so no XCD takes the longest item of every round).
+        // The odd-numbered XCDs stream K/V about 10% slower than the even ones, so after
+        // every kOddRounds rounds one round of 4 items goes to the even XCDs alone: per
+        // cycle of kOddRounds * 8 + 4 items an even XCD takes kOddRounds + 1, an odd one
+        // kOddRounds.  Past the list: done.
         const int x = v % kXcds, r = v / kXcds;
         const int rd = r / num_kv_heads;
-        i = rd * kXcds + ((rd & 1) ? kXcds - 1 - x : x);
+        const int per = (x & 1) ? kOddRounds : kOddRounds + 1;  // this XCD's items per cycle
+        const int cyc = rd / per, k = rd - cyc * per;
+        const int base = cyc * (kOddRounds * kXcds + kXcds / 2);
+        i = k < kOddRounds ? base + k * kXcds + ((k & 1) ? kXcds - 1 - x : x)
+                           : base + kOddRounds * kXcds + x / 2;
         h = r % num_kv_heads;
         if (i >= live) return;
       }
