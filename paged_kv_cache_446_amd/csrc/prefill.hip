@@ -164,20 +164,32 @@ struct PfLayout {
   }
 };
 
+// Queue counters of the tiled kernel (ints at the workspace's queue offset): the
+// next-item counter of each die, the number of items and the number of merges.
+constexpr int kPfQNext = 0;
+constexpr int kPfQTotal = kXcds;
+constexpr int kPfQMerges = kXcds + 1;
+
 // Work list of the tiled kernel: one workgroup of 1024 threads.  Every
 // (sequence, q-tile) of a chunk wider than small_cols columns has one item per
-// KV head; items are ordered by the context they read, longest first, in
-// 1024-token classes.  The (sequence, q-tile) pairs are first listed flat
-// (a scan over the sequences), so that the threads share them evenly however
-// they are spread over sequences.
+// KV head, the KV heads of a q-tile side by side; items are ordered by the
+// context they read, longest first, in 1024-token classes.  The (sequence,
+// q-tile) pairs are first listed flat (a scan over the sequences), so that the
+// threads share them evenly however they are spread over sequences.  All
+// q-tiles of a sequence take the class of its whole context, so that the lanes
+// holding them reserve one range together: its q-tiles sit next to each other.
+// The tiled kernel's workgroups on die d take items d, d + 8, d + 16, ... first:
+// with Hkv a multiple of 8 those are all of KV heads d, d + 8, ..., so the
+// q-tiles of one (sequence, KV head), which read nearly the same blocks, run at
+// about the same time on one die and share its L2.
 //
 // Splitting: with W the blocks all items read (over KV heads too) and P the
 // workers, an item of b blocks is cut into np = floor(b P / W) pieces (at least
 // one, each at least kPfMinPiece blocks and a whole number of pipeline steps of
 // sb blocks): items of more than one worker's share are split, and the pieces
 // of all split items number at most P, so one round of workers takes them and
-// max_slots >= P partial slots suffice.  Also resets the queue: queue[0] = next
-// item, queue[1] = number of items, queue[2] = number of merges.
+// max_slots >= P partial slots suffice.  Pieces keep the class of their own
+// length.  Also resets the queue counters.
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl, int num_seqs,
     int num_kv_heads, int G, int cols, int small_cols, int bt_stride, int sb, int workers,
@@ -265,9 +277,12 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
         for (int h = 0; h < num_kv_heads; ++h)
           merges[mi + h] = PfMerge{s, qb, q_len, t, h, np, slot0 + h * np, 0};
       }
+      const int n = seq_lens[s];
+      const int vb_seq = n > 0 ? min((n - 1) / kBlock + 1, bt_stride) : 0;  // the last q-tile's
       for (int p = 0; p < np; ++p) {
         const int kb0 = p * pl, kb1 = min(vb, kb0 + pl);
-        const int b = kPfBuckets - 1 - min(kPfBuckets - 1, ((kb1 - kb0) * kBlock) >> 10);
+        const int len = np > 1 ? kb1 - kb0 : vb_seq;
+        const int b = kPfBuckets - 1 - min(kPfBuckets - 1, (len * kBlock) >> 10);
         const int at = atomicAdd(&hist[b], num_kv_heads);
         if (pass == 1)
           for (int h = 0; h < num_kv_heads; ++h)
@@ -284,12 +299,12 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
         run += hist[b];
         hist[b] = 0;
       }
-      queue[0] = 0;
-      queue[1] = min(run, max_items);
+      for (int d = 0; d < kXcds; ++d) queue[kPfQNext + d] = 0;
+      queue[kPfQTotal] = min(run, max_items);
     }
     __syncthreads();
   }
-  if (tid == 0) queue[2] = sm_merge;
+  if (tid == 0) queue[kPfQMerges] = sm_merge;
 }
 
 template <class DT, int D, int G>
@@ -319,15 +334,30 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
   const int w = uniform(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int hq = num_kv_heads * G;
-  const int total = queue[1];
+  const int total = queue[kPfQTotal];
   const int64_t blk_elems = (int64_t)num_kv_heads * Gm::kTile;
+  // workgroups are dealt to the dies round-robin: this one takes its die's share of the list
+  // (items die, die + 8, ...) first, then the other dies' shares in turn (thread 0 only)
+  const int die = blockIdx.x % kXcds;
+  int tried = 0;
 
   for (;;) {
-    if (tid == 0) sm_item = atomicAdd(&queue[0], 1);
+    if (tid == 0) {
+      int got = -1;
+      for (; tried < kXcds; ++tried) {
+        const int d = (die + tried) % kXcds;
+        const int i = atomicAdd(&queue[kPfQNext + d], 1) * kXcds + d;
+        if (i < total) {
+          got = i;
+          break;
+        }
+      }
+      sm_item = got;
+    }
     __syncthreads();
     const int it = sm_item;
     __syncthreads();
-    if (it >= total) break;
+    if (it < 0) break;
     const PfItem item = items[it];
     const int s = item.s, h = item.h, kb0 = item.kb0, kb1 = item.kb1;
     const int qb = qsl[s], q_len = qsl[s + 1] - qb, n = seq_lens[s];
@@ -566,7 +596,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   constexpr int QT = PfGeo<DT, D>::kCols / G;  // query tokens per q-tile
   constexpr int kQuads = D / 4;
   constexpr int kGroups = kPfSlotCols / kMergeCols;
-  const int j = xcd_unit(blockIdx.x, queue[2] * kGroups);
+  const int j = xcd_unit(blockIdx.x, queue[kPfQMerges] * kGroups);
   if (j < 0) return;
   const PfMerge mg = merges[j / kGroups];
   const int c0 = (j % kGroups) * kMergeCols;
