@@ -177,11 +177,14 @@ constexpr int kPfQMerges = kXcds + 1;
 // q-tile) pairs are first listed flat (a scan over the sequences), so that the
 // threads share them evenly however they are spread over sequences.  All
 // q-tiles of a sequence take the class of its whole context, so that the lanes
-// holding them reserve one range together: its q-tiles sit next to each other.
-// The tiled kernel's workgroups on die d take items d, d + 8, d + 16, ... first:
-// with Hkv a multiple of 8 those are all of KV heads d, d + 8, ..., so the
-// q-tiles of one (sequence, KV head), which read nearly the same blocks, run at
-// about the same time on one die and share its L2.
+// holding them reserve one range together: its q-tiles sit next to each other,
+// listed last q-tile (the longest) first.
+// The tiled kernel's workgroups on die d take items d, d + 8, d + 16, ... first.
+// A (sequence, q-tile, piece) lists its KV heads rotated by (sequence + piece),
+// so that with Hkv a multiple of 8 the q-tiles of one (sequence, KV head,
+// piece), which read nearly the same blocks, all fall to one die and run there
+// at about the same time, sharing its L2, while each die still sees every KV
+// head.
 //
 // Splitting: with W the blocks all items read (over KV heads too) and P the
 // workers, an item of b blocks is cut into np = floor(b P / W) pieces (at least
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
   int pos = before + x - mine;
   for (int j = 0; j < k && s0 + j < num_seqs; ++j) {
     const int nt = ntiles(s0 + j);
-    for (int t = 0; t < nt; ++t) tiles[pos + t] = int2{s0 + j, t};
+    for (int t = 0; t < nt; ++t) tiles[pos + t] = int2{s0 + j, nt - 1 - t};  // longest first
     pos += nt;
   }
   __syncthreads();  // the list is visible to the whole workgroup
@@ -284,11 +287,14 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(
         const int len = np > 1 ? kb1 - kb0 : vb_seq;
         const int b = kPfBuckets - 1 - min(kPfBuckets - 1, (len * kBlock) >> 10);
         const int at = atomicAdd(&hist[b], num_kv_heads);
-        if (pass == 1)
-          for (int h = 0; h < num_kv_heads; ++h)
-            if (base[b] + at + h < max_items)
-              items[base[b] + at + h] =
-                  PfItem{s, t, h, kb0, kb1, np > 1 ? slot0 + h * np + p : -1, 0, 0};
+        if (pass == 1) {
+          const int rot = (s + p) % num_kv_heads;  // same for every q-tile of (s, piece p)
+          for (int h = 0; h < num_kv_heads; ++h) {
+            const int at_h = base[b] + at + (h + rot) % num_kv_heads;
+            if (at_h < max_items)
+              items[at_h] = PfItem{s, t, h, kb0, kb1, np > 1 ? slot0 + h * np + p : -1, 0, 0};
+          }
+        }
       }
     }
     __syncthreads();
@@ -336,9 +342,13 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
   const int hq = num_kv_heads * G;
   const int total = queue[kPfQTotal];
   const int64_t blk_elems = (int64_t)num_kv_heads * Gm::kTile;
-  // workgroups are dealt to the dies round-robin: this one takes its die's share of the list
-  // (items die, die + 8, ...) first, then the other dies' shares in turn (thread 0 only)
-  const int die = blockIdx.x % kXcds;
+  // With at least two rounds of items, workgroups (dealt to the dies round-robin) take their
+  // die's share of the list (items die, die + 8, ...) first, then the other dies' shares in
+  // turn; with fewer, every workgroup starts at once and nothing is gained by keeping the
+  // q-tiles of one context on one die (they then read the same lines at the same moment),
+  // so all take the list in order.  Thread 0 only.
+  const bool by_die = total >= 2 * (int)gridDim.x;
+  const int die = by_die ? blockIdx.x % kXcds : 0;
   int tried = 0;
 
   for (;;) {
@@ -346,11 +356,13 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
       int got = -1;
       for (; tried < kXcds; ++tried) {
         const int d = (die + tried) % kXcds;
-        const int i = atomicAdd(&queue[kPfQNext + d], 1) * kXcds + d;
+        const int k = atomicAdd(&queue[kPfQNext + d], 1);
+        const int i = by_die ? k * kXcds + d : k;
         if (i < total) {
           got = i;
           break;
         }
+        if (!by_die) tried = kXcds - 1;  // the one list is done
       }
       sm_item = got;
     }
