@@ -166,3 +166,39 @@ def test_decode_units_beyond_the_grid_cap(kind):
     gp.attention(run)
     torch.cuda.synchronize()
     assert np.array_equal(bits, run.out_bits())
+
+
+@pytest.mark.parametrize("hkv", [1, 2, 4, 8])
+def test_prefill_list_of_several_rounds_taken_die_by_die(hkv):
+    # Prefill lists of at least two rounds of items (two per resident workgroup) are
+    # taken die by die, each die's workgroups first taking items d, d + 8, ... and then
+    # the other dies' shares; here 512 q-tiles per KV head (32 chunks of 1,024 tokens,
+    # 64-token q-tiles at 4 query heads per KV head) plus one chunk over a 40,000-token
+    # context, whose q-tiles the plan cuts into pieces.  With fewer than 8 KV heads a
+    # die's share mixes heads.  Sampled rows (the long chunk among them) against the
+    # oracle, every row finite, a second call the same bits.
+    import torch
+
+    from tests import gpu_pipeline as gp
+
+    rng = np.random.default_rng([446, 104, hkv])
+    ctx = rng.integers(0, 256, size=33, endpoint=True)
+    q = np.full(33, 1024, dtype=np.int64)
+    ctx[17], q[17] = 40000, 256
+    spec = workloads.make_spec(f"rounds{hkv}", (446, 104, hkv), "bf16", 4 * hkv, hkv, 64, ctx, q)
+    gp.log(f"[rounds] Hkv={hkv}: S={spec.num_seqs} query={spec.num_q_tokens} "
+           f"context={int(spec.seq_lens.sum())}")
+    run = gp.prepare(spec)
+    bits = run.out_bits().copy()
+    got = numerics.to_f64(bits, spec.dtype).reshape(spec.num_q_tokens, spec.num_q_heads, spec.head_dim)
+    seqs = sorted({17, int(np.argmin(spec.seq_lens))} |
+                  set(int(s) for s in rng.choice(33, size=3, replace=False)))
+    ref = op.run(spec, seqs=seqs)
+    rows = np.concatenate([np.arange(spec.query_start_loc[s], spec.query_start_loc[s + 1]) for s in seqs])
+    ok, worst = gp.compare(got[rows], ref.out[rows], spec.dtype)
+    gp.log(f"[rounds] Hkv={hkv}: {len(seqs)} sequences, {len(rows)} rows, worst {worst:.3g}")
+    assert ok, f"Hkv={hkv}: worst error {worst}"
+    assert np.isfinite(got).all()
+    gp.attention(run)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits, run.out_bits())
