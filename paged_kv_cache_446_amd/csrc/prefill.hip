@@ -8,10 +8,12 @@
 //
 //   * 16-bit types: a plan kernel lists (sequence, 256-column query tile, KV
 //     head, block range) items, longest first, and a persistent kernel takes
-//     them from a queue.  Per item, K/V tiles of several blocks at a time are
-//     staged in LDS (double buffered) and shared by 8 wavefronts of 32
-//     columns; the scores S^T = K.Q^T use 16x16x32 matrix instructions and the
-//     product O^T += V^T.P^T runs over 32 tokens at a time, also 16x16x32.
+//     them from a queue, die by die when the list is long (the query tiles
+//     reading one context then share a die's L2).  Per item, K/V tiles of
+//     several blocks at a time are staged in LDS (double buffered) and shared
+//     by 8 wavefronts of 32 columns; the scores S^T = K.Q^T use 16x16x32
+//     matrix instructions and the product O^T += V^T.P^T runs over 32 tokens
+//     at a time, also 16x16x32.
 //     When a few long items would leave most of the chip idle, the plan cuts
 //     their context into pieces of about one workgroup's share of the work;
 //     pieces write fp32 partials (max, sum, normalised output) and a merge
