@@ -476,9 +476,11 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
           sc[b][ct] = a;
         }
       }
-      // column maxima of this step; the reference max moves only when one of them exceeds it
-      // by more than kPfLag (a wave-wide decision)
-      float bms[kCT];
+      // the reference max moves only when some column's max over this step exceeds it by
+      // more than kPfLag (a wave-wide decision); a lane's own max decides it (x * scale rounds
+      // monotonically, so some lane's scaled max exceeds the bound exactly when the column's
+      // does), and the column maxima are reduced across lanes only when it moves
+      float bml[kCT];
       bool move = false;
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
@@ -495,13 +497,13 @@ void prefill_tiled_kernel(const typename DT::T* __restrict__ q, typename DT::T* 
 #pragma unroll
         for (int b = 0; b < kSB; ++b)
           bm = fmaxf(bm, fmaxf(fmaxf(sc[b][ct][0], sc[b][ct][1]), fmaxf(sc[b][ct][2], sc[b][ct][3])));
-        bms[ct] = col_max4(bm) * scale_log2;
-        move |= bms[ct] > m[ct] + kPfLag;  // also the first visible key of a column (m = -inf)
+        bml[ct] = bm;
+        move |= bm * scale_log2 > m[ct] + kPfLag;  // also the first visible key (m = -inf)
       }
       if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct) {
-          const float mn = fmaxf(m[ct], bms[ct]);
+          const float mn = fmaxf(m[ct], col_max4(bml[ct]) * scale_log2);
           const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[ct] - mn);
 #pragma unroll
           for (int nn = 0; nn < Gm::kN; ++nn) acc[ct][nn] *= alpha;
