@@ -67,6 +67,15 @@ def algorithmic_bytes(spec):
     return kv, kv + qo + table
 
 
+def prefill_flops(spec, rows):
+    """Matrix FLOPs the method must do for the chunks of ``rows``: per query head, 2 D for
+    the score and 2 D for the weighted V of every visible (query token, key) pair; row i
+    of a chunk over ctx cached tokens sees ctx + i + 1 keys (masked pairs not counted)."""
+    q = spec.q_lens[rows].astype(np.int64)
+    ctx = spec.seq_lens[rows].astype(np.int64) - q
+    return int((4 * spec.num_q_heads * spec.head_dim * (q * ctx + q * (q + 1) // 2)).sum())
+
+
 class ContiguousPlacer:
     """Storage without paging, for the paging-overhead comparison: every sequence
     gets one run of consecutive blocks sized for its final length, in sequence
@@ -644,10 +653,7 @@ def main():
             pev.append((ea, eb))
         torch.cuda.synchronize()
         pf_ms = float(np.mean([a.elapsed_time(b) for a, b in pev]))
-        ctx = spec.seq_lens[pf_rows].astype(np.int64) - pq_lens
-        # masked (token, key) pairs not counted: row i of a chunk sees ctx + i + 1 keys
-        flops = int((4 * spec.num_q_heads * spec.head_dim *
-                     (pq_lens * ctx + pq_lens * (pq_lens + 1) // 2)).sum())
+        flops = prefill_flops(spec, pf_rows)
         tflops = flops / (pf_ms * 1e-3) / 1e12
         prefill = {
             "kernel": "paged_attention over the batch's prefill chunks alone (prefill plan + "
